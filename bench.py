@@ -1,0 +1,220 @@
+"""Throughput of the Sparse Delta Memory hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+product-key addressing (sdm_score_topk) for every token of every (b,h) stream,
+then the sparse gated-delta scan (sdm_scan) over the same tokens.  The memory
+table is carried from step to step (each step continues the recurrence, like
+the next chunk of a long sequence; the work per step is identical).
+
+Default workload: the large N = 2^20 configuration (B=8, H=8, T=4096,
+d_k=128, n_sub=1024, d_v=64, W=R=64, bf16 projections, fp32 table of 17 GB).
+
+Prints ONE JSON line with the throughput in stream-tokens/s (tokens of all
+B*H streams per second), a roofline object for the dominant kernel (the scan)
+and a CPU baseline (the oracle on a bounded sample of the same workload).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config large]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SDM tokens/sec (all B·H streams) at N=2^20; scan HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak
+
+
+def scan_bytes_per_token(wl):
+    """Algorithmic scan bytes per stream-token: W rows read and written, R rows
+    read, d_v fp32 each."""
+    return (2 * wl.W + wl.R) * wl.d_v * 4
+
+
+def score_bytes_per_token(wl):
+    """Algorithmic addressing/stream bytes per stream-token: q', k' read,
+    (idx, weight) of W + R slots written by the addressing and read by the
+    scan, v and the two gates read, the output row written."""
+    e = 2 if wl.bf16 else 4
+    return 2 * wl.d_k * e + 2 * (wl.W + wl.R) * 8 + wl.d_v * e + 8 + wl.d_v * 4
+
+
+def cpu_baseline(wl, x, n_streams):
+    """Oracle (single thread) on the first n_streams streams, all tokens."""
+    import oracle
+    import synth
+    tok = 0
+    t_total = 0.0
+    for s in range(n_streams):
+        b, h = divmod(s, wl.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        m0 = synth.to_numpy(x["m0_cpu"][s]) if "m0_cpu" in x else None
+        hq = synth.to_numpy(x["q"][sl])
+        hk = synth.to_numpy(x["k"][sl])
+        hc = synth.to_numpy(x["subkeys"][h:h + 1])
+        hv = synth.to_numpy(x["v"][sl])
+        ha = synth.to_numpy(x["alpha"][sl])
+        hb = synth.to_numpy(x["beta"][sl])
+        M = m0[None, None].copy()
+        t0 = time.perf_counter()
+        r = oracle.score_topk(hq, hk, hc, wl.W, wl.R)
+        oracle.scan(M, r["widx"], r["wwt"], r["ridx"], r["rwt"], hv, ha, hb)
+        t_total += time.perf_counter() - t0
+        tok += wl.T
+    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_streams} of {wl.streams} streams x all {wl.T} tokens "
+                      f"({tok} stream-tokens), addressing + scan, single-threaded fp32 C"}
+
+
+def cpu_baseline_gdn(wl, x, n_streams):
+    import numpy as np
+    import oracle
+    import synth
+    tok, t_total = 0, 0.0
+    for s in range(n_streams):
+        b, h = divmod(s, wl.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        S = np.zeros((1, 1, wl.d_v, wl.d_k), np.float32)
+        args = [synth.to_numpy(x[n][sl]) for n in ("k", "q", "v", "alpha", "beta")]
+        t0 = time.perf_counter()
+        oracle.gdn_scan(S, *args)
+        t_total += time.perf_counter() - t0
+        tok += wl.T
+    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_streams} of {wl.streams} streams x all {wl.T} tokens "
+                      f"({tok} stream-tokens), single-threaded fp32 C"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="large", choices=["tiny", "mid", "large", "long", "gdn"])
+    ap.add_argument("--cpu-streams", type=int, default=None,
+                    help="streams in the oracle CPU-baseline sample (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "see DESIGN.md for how the path would shard across GPUs.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_addressed_linear_amd as sdm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sdm.lib()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.config]
+
+    print(f"[bench] workload {wl.name}: generating inputs on the device", file=sys.stderr,
+          flush=True)
+    x = synth.make_inputs(wl, device=dev)
+    dense = wl.dense
+    n_cpu = args.cpu_streams if args.cpu_streams is not None else (2 if dense else 8)
+    n_cpu = min(n_cpu, wl.streams)
+    if not dense and n_cpu:
+        # initial tables of the CPU sample, taken before the GPU steps modify M
+        x["m0_cpu"] = [x["m0"][s // wl.H, s % wl.H].cpu() for s in range(n_cpu)]
+
+    stream = torch.cuda.current_stream()
+    if dense:
+        S = x["s0"]
+        out = torch.empty((wl.B, wl.H, wl.T, wl.d_v), device=dev)
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            sdm.gdn_scan(S, x["k"], x["q"], x["v"], x["alpha"], x["beta"], out=out)
+            if ev:
+                ev[1].record(stream)
+    else:
+        M = x["m0"]
+        B, H, T = wl.B, wl.H, wl.T
+        idx_bufs = (torch.empty((B, H, T, wl.W), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, T, wl.W), device=dev),
+                    torch.empty((B, H, T, wl.R), dtype=torch.int32, device=dev),
+                    torch.empty((B, H, T, wl.R), device=dev))
+        out = torch.empty((B, H, T, wl.d_v), device=dev)
+        need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
+        work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            sdm.score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R, out=idx_bufs)
+            if ev:
+                ev[1].record(stream)
+            sdm.scan(M, *idx_bufs, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
+            if ev:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    nev = 2 if dense else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+    ms_wall = wall * 1e3 / args.steps
+    stream_tokens = wl.streams * wl.T
+    value = stream_tokens / (ms_wall * 1e-3)
+
+    if dense:
+        ms_k = ms_step
+        flops = wl.streams * wl.T * (4 * wl.d_v * wl.d_k * 2)  # 4 d_v d_k FMA per token
+        achieved = flops / (ms_k * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": "sdm_gdn_kernel", "achieved": round(achieved, 2),
+                "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                "ms": round(ms_k, 4), "work_per_launch": flops}
+        kernels = {"gdn_ms": round(ms_k, 4)}
+    else:
+        ms_score = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        ms_scan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        sbytes = stream_tokens * scan_bytes_per_token(wl)
+        achieved = sbytes / (ms_scan * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
+        allb = stream_tokens * (scan_bytes_per_token(wl) + score_bytes_per_token(wl))
+        kernels = {"score_topk_ms": round(ms_score, 4), "scan_ms": round(ms_scan, 4),
+                   "step_GBps_all_traffic": round(allb / (ms_step * 1e-3) / 1e9, 1)}
+
+    cpu = None
+    if n_cpu:
+        print(f"[bench] CPU baseline: oracle on {n_cpu} streams", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_gdn(wl, x, n_cpu) if dense else cpu_baseline(wl, x, n_cpu)
+
+    cfg = {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d_k": wl.d_k, "d_v": wl.d_v}
+    if not dense:
+        cfg.update({"n_sub": wl.n_sub, "N": wl.N, "W": wl.W, "R": wl.R,
+                    "inputs": "bf16" if wl.bf16 else "fp32", "table": "fp32",
+                    "table_GB": round(wl.table_bytes() / 1e9, 2)})
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "kernels": kernels, "ms_per_step_events": round(ms_step, 4)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

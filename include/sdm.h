@@ -1,0 +1,165 @@
+/*
+ * sdm.h -- C ABI of libsdm, the MI355X (gfx950) Sparse Delta Memory hot path.
+ *
+ * Sparse Delta Memory (SDM) replaces the small dense state of a gated
+ * DeltaNet layer with an explicit table M of N = n_sub^2 rows of d_v floats
+ * per (batch, head) stream, addressed through product keys.  Source of the
+ * method: the gist.science technical summaries of paper 2607.07386, "Sparse
+ * Delta Memory" (Spanish page, section "Mecanismo Central", items 1-4, and
+ * section "Diseno IsoFLOP"; French page, section "Mecanisme Central").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (HBM of the current HIP device)
+ *    owned by the caller; the library never allocates, frees or copies
+ *    caller memory and never synchronises the host.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and the call returns at once; results are ready
+ *    when the stream reaches that point.  Calls are stateless and reentrant.
+ *  - Tensors are dense, row-major (C order), with the shapes given below and
+ *    no padding.  Addresses must be 16-byte aligned.  When T == 0 the tensors
+ *    with a T axis hold no elements and their pointers may be NULL.
+ *  - Arguments are validated on the host before anything is enqueued.  On a
+ *    nonzero return nothing has been enqueued and no output was written.
+ *    SDM_ERR_HIP reports a failed launch; faults inside a kernel surface at
+ *    the caller's next synchronisation, as with any HIP kernel.
+ *  - Inputs are assumed finite.  NaN scores give unspecified selections.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDM_OK = 0,
+  SDM_ERR_NULL = 1,        /* a required pointer is NULL */
+  SDM_ERR_SHAPE = 2,       /* sizes inconsistent (odd d_k, W > N, N >= 2^31, ...) */
+  SDM_ERR_DTYPE = 3,       /* unknown element type */
+  SDM_ERR_UNSUPPORTED = 4, /* valid problem outside this build's kernel limits */
+  SDM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  SDM_ERR_HIP = 6,         /* a HIP launch or runtime call failed */
+  SDM_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */
+} sdm_status;
+
+typedef enum {
+  SDM_F32 = 0,  /* IEEE binary32 */
+  SDM_BF16 = 1  /* bfloat16 (upper half of a binary32), widened exactly to fp32 */
+} sdm_dtype;
+
+/* Sizes of one SDM problem.  N = n_sub * n_sub slots per stream.
+ * B batches x H heads = B*H independent streams of T tokens each. */
+typedef struct {
+  int32_t B, H, T;   /* batch, heads, tokens per stream */
+  int32_t d_k;       /* projected key/query width (even); halves of d_k/2 */
+  int32_t n_sub;     /* sub-keys per half */
+  int32_t d_v;       /* value width = row width of M */
+  int32_t W, R;      /* write and read slots per token */
+} sdm_dims;
+
+/*
+ * sdm_score_topk -- product-key addressing (Spanish page "Mecanismo Central"
+ * item 2; French page "Mecanisme Central", "Selection de Cles Creuses").
+ *
+ * For each token of each stream (b,h), the projected key k' and query q' are
+ * cut into halves x1 = x[0:d_k/2) and x2 = x[d_k/2:d_k).  Each half is scored
+ * against its own sub-key table of head h:  s_c[i] = <x_c, C[h][c][i]>.  The
+ * score of slot s = i*n_sub + j is s_1[i] + s_2[j].  The W best slots of k'
+ * (write set) and the R best slots of q' (read set) are found with the
+ * two-stage identity topk(s1 (+) s2) = topk(topk(s1) (+) topk(s2)); the
+ * N-vector of slot scores is never formed.  Order: score descending, ties to
+ * the lower index at both stages.  Weights: softmax (temperature 1) over the
+ * selected slot scores, separately for the write and read sets.
+ *
+ *   qp, kp   [B][H][T][d_k]        in_dtype   projected query / key
+ *   subkeys  [H][2][n_sub][d_k/2]  in_dtype   shared by queries and keys
+ *   widx     [B][H][T][W]  int32   out: write slots, rank order
+ *   wwt      [B][H][T][W]  fp32    out: write weights
+ *   ridx     [B][H][T][R]  int32   out: read slots, rank order
+ *   rwt      [B][H][T][R]  fp32    out: read weights
+ *
+ * Scores are accumulated in fp32 (bf16 products are exact in fp32).
+ * Kernel limits (else SDM_ERR_UNSUPPORTED): n_sub <= 1024, d_k/2 a
+ * multiple of 16 and <= 256, W, R <= min(n_sub, 128).
+ */
+int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, const void* kp,
+                   const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
+                   void* stream);
+
+/*
+ * sdm_scan -- sparse gated-delta write and sparse read over the memory table
+ * (Spanish page "Mecanismo Central" items 1, 3 and 4; French page
+ * "Mecanisme Central").
+ *
+ * For every stream, tokens t = 0..T-1 in order:
+ *   write: for each of the W write slots s with weight w, c = beta_t * w,
+ *          M[s] <- (1 - c) * (alpha_t * M[s]) + c * v_t
+ *          (= m~ + beta_t w (v_t - m~) with m~ = alpha_t M[s]), each product
+ *          and the sum rounded separately in fp32; every other row is left
+ *          bit-for-bit unchanged;
+ *   read:  out_t = sum over the R read slots s of r_s * M[s], using the rows
+ *          as they are AFTER token t's write.
+ *
+ *   M        [B][H][N][d_v]  fp32        in/out: memory table (M0 in, M_T out)
+ *   widx/wwt [B][H][T][W]    int32/fp32  write slots (distinct within a token)
+ *   ridx/rwt [B][H][T][R]    int32/fp32  read slots
+ *   v        [B][H][T][d_v]  v_dtype
+ *   alpha    [B][H][T]       fp32        forget gate
+ *   beta     [B][H][T]       fp32        write strength
+ *   out      [B][H][T][d_v]  fp32        output
+ *   workspace                            device scratch of at least
+ *                                        sdm_scan_workspace_size(dims) bytes
+ *                                        (may be NULL when that size is 0);
+ *                                        its contents on entry do not matter.
+ *
+ * Slot indices must lie in [0, N) and the W write slots of one token must be
+ * distinct; neither is checked on the device (an index outside [0, N) reads
+ * and writes outside the stream's table).  Results are deterministic: the
+ * read sums use a fixed order.  Scanning [0,T1) and then [T1,T) with the same
+ * M equals one scan of [0,T).  Two calls that overlap on one device must not
+ * share M, out or workspace.
+ * Kernel limits (else SDM_ERR_UNSUPPORTED): d_v a multiple of 16 and <= 512,
+ * W, R <= 256.
+ */
+int sdm_scan(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int32_t* widx,
+             const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+             const float* alpha, const float* beta, float* out, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sdm_scan needs for these sizes (0 when none, or
+ * when the sizes are invalid).  Pure host function. */
+size_t sdm_scan_workspace_size(const sdm_dims* dims);
+
+/*
+ * sdm_gdn_scan -- the dense gated DeltaNet recurrence that SDM extends
+ * (Spanish page "Planteamiento del Problema", "Metodologia"; its state
+ * starts at zero, "Estado Inicial Aprendido"), used as the IsoFLOP baseline:
+ *   S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,
+ *   out_t = S_t q_t  (read after the update).
+ *
+ *   S        [B][H][d_v][d_k]  fp32   in/out: state (maps k to v)
+ *   k, q     [B][H][T][d_k]    dtype
+ *   v        [B][H][T][d_v]    dtype
+ *   alpha, beta [B][H][T]      fp32
+ *   out      [B][H][T][d_v]    fp32
+ *
+ * Kernel limits (else SDM_ERR_UNSUPPORTED): d_k = d_v = 128.
+ */
+int sdm_gdn_scan(int32_t B, int32_t H, int32_t T, int32_t d_k, int32_t d_v, sdm_dtype dtype,
+                 float* S, const void* k, const void* q, const void* v, const float* alpha,
+                 const float* beta, float* out, void* stream);
+
+/* Static string naming a status code. */
+const char* sdm_status_str(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char* sdm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDM_H */

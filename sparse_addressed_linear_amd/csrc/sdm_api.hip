@@ -1,0 +1,163 @@
+// C ABI of libsdm: argument validation and dispatch.  Every pointer is a
+// caller-owned device pointer; nothing is allocated or synchronised here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sdm.h"
+#include "sdm_internal.h"
+
+namespace sdm {
+size_t score_topk_lds_bytes(int n_sub, int W, int R);
+}
+
+namespace {
+
+constexpr int64_t kMaxN = 0x7fffffffLL;
+constexpr size_t kMaxLds = 160 * 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const sdm_dims* d) {
+  if (d->B < 1 || d->H < 1 || d->T < 0 || d->d_k < 2 || (d->d_k & 1) || d->n_sub < 1 ||
+      d->d_v < 1)
+    return SDM_ERR_SHAPE;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  if (N > kMaxN) return SDM_ERR_SHAPE;
+  if (d->W < 1 || d->W > N || d->R < 1 || d->R > N) return SDM_ERR_SHAPE;
+  if ((int64_t)d->B * d->H > 0x7fffffffLL) return SDM_ERR_SHAPE;
+  return SDM_OK;
+}
+
+bool valid_dtype(int t) { return t == SDM_F32 || t == SDM_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                   const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
+                   void* stream) {
+  if (!d || !subkeys) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  // tensors with a T axis have no elements when T == 0 and may then be NULL
+  if (d->T > 0 && (!qp || !kp || !widx || !wwt || !ridx || !rwt)) return SDM_ERR_NULL;
+  if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
+  const int dh = d->d_k / 2;
+  if (d->n_sub > 1024 || dh % 16 != 0 || dh > 256 || d->W > d->n_sub || d->R > d->n_sub ||
+      d->W > 128 || d->R > 128)
+    return SDM_ERR_UNSUPPORTED;
+  if (sdm::score_topk_lds_bytes(d->n_sub, d->W, d->R) > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  if (!aligned16(qp) || !aligned16(kp) || !aligned16(subkeys) || !aligned16(widx) ||
+      !aligned16(wwt) || !aligned16(ridx) || !aligned16(rwt))
+    return SDM_ERR_ALIGN;
+  if (d->T == 0) return SDM_OK;
+  sdm::ScoreArgs a{};
+  a.qp = qp;
+  a.kp = kp;
+  a.subkeys = subkeys;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.S = d->B * d->H;
+  a.H = d->H;
+  a.T = d->T;
+  a.d_k = d->d_k;
+  a.n_sub = d->n_sub;
+  a.W = d->W;
+  a.R = d->R;
+  hipError_t e = sdm::launch_score_topk(a, in_dtype == SDM_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+size_t sdm_scan_workspace_size(const sdm_dims* d) {
+  if (!d || check_dims(d) != SDM_OK) return 0;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  return sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R).work_bytes;
+}
+
+int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
+             const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+             const float* alpha, const float* beta, float* out, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (!d || !M) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (d->T > 0 && (!widx || !wwt || !ridx || !rwt || !v || !alpha || !beta || !out))
+    return SDM_ERR_NULL;
+  if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
+  if (d->d_v % 16 != 0 || d->d_v > 512 || d->W > 256 || d->R > 256) return SDM_ERR_UNSUPPORTED;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  const sdm::ScanPlan p = sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
+  if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
+    return SDM_ERR_WORKSPACE;
+  if (!aligned16(M) || !aligned16(v) || !aligned16(out) || (p.work_bytes && !aligned16(workspace)))
+    return SDM_ERR_ALIGN;
+  if (d->T == 0) return SDM_OK;
+  sdm::ScanArgs a{};
+  a.M = M;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.work = static_cast<float*>(workspace);
+  a.N = N;
+  a.S = d->B * d->H;
+  a.T = d->T;
+  a.d_v = d->d_v;
+  a.W = d->W;
+  a.R = d->R;
+  hipError_t e = sdm::launch_scan(a, p, v_dtype == SDM_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+int sdm_gdn_scan(int32_t B, int32_t H, int32_t T, int32_t d_k, int32_t d_v, sdm_dtype dtype,
+                 float* S, const void* k, const void* q, const void* v, const float* alpha,
+                 const float* beta, float* out, void* stream) {
+  if (!S) return SDM_ERR_NULL;
+  if (B < 1 || H < 1 || T < 0 || d_k < 1 || d_v < 1) return SDM_ERR_SHAPE;
+  if (T > 0 && (!k || !q || !v || !alpha || !beta || !out)) return SDM_ERR_NULL;
+  if (!valid_dtype(dtype)) return SDM_ERR_DTYPE;
+  if (d_k != 128 || d_v != 128) return SDM_ERR_UNSUPPORTED;
+  if (!aligned16(S) || !aligned16(k) || !aligned16(q) || !aligned16(v) || !aligned16(out))
+    return SDM_ERR_ALIGN;
+  if (T == 0) return SDM_OK;
+  sdm::GdnArgs a{};
+  a.S = S;
+  a.k = k;
+  a.q = q;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.nS = B * H;
+  a.T = T;
+  a.d_k = d_k;
+  a.d_v = d_v;
+  hipError_t e = sdm::launch_gdn(a, dtype == SDM_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+const char* sdm_status_str(int s) {
+  switch (s) {
+    case SDM_OK: return "ok";
+    case SDM_ERR_NULL: return "null pointer";
+    case SDM_ERR_SHAPE: return "inconsistent sizes";
+    case SDM_ERR_DTYPE: return "unknown element type";
+    case SDM_ERR_UNSUPPORTED: return "outside this build's kernel limits";
+    case SDM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SDM_ERR_HIP: return "HIP launch failed";
+    case SDM_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* sdm_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal declarations shared by the libsdm translation units (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sdm {
+
+// Workgroups the scan aims to spread one launch over (one per CU of a
+// 256-CU MI355X).
+constexpr int kTargetWorkgroups = 256;
+
+// Orders a wave's earlier LDS writes before its later LDS reads by other
+// lanes of the same wave (code-motion barrier plus wavefront-scope fence).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct ScanArgs {
+  float* M;                // [S][N][d_v]
+  const int32_t* widx;     // [S][T][W]
+  const float* wwt;
+  const int32_t* ridx;     // [S][T][R]
+  const float* rwt;
+  const void* v;           // [S][T][d_v]
+  const float* alpha;      // [S][T]
+  const float* beta;
+  float* out;              // [S][T][d_v]
+  float* work;             // [P][S][T][d_v] partial reads (P > 1)
+  int64_t N;
+  int32_t S, T, d_v, W, R;
+  int32_t CS, P, hsize, lcap, xcd_map;
+};
+
+struct ScanPlan {
+  int lpr;      // lanes per row slice (slice = 4*lpr columns)
+  int CS;       // column slices per stream
+  int P;        // slot partitions
+  int nw;       // waves per workgroup = tokens per block
+  int hsize;    // LDS hash size (power of two)
+  int lcap;     // per-wave event list capacity
+  size_t lds;   // dynamic LDS bytes
+  size_t work_bytes;
+};
+
+ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R);
+hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, bool vbf16, hipStream_t stream);
+
+struct ScoreArgs {
+  const void* qp;          // [S][T][d_k]
+  const void* kp;
+  const void* subkeys;     // [H][2][n_sub][dh]
+  int32_t* widx;           // [S][T][W]
+  float* wwt;
+  int32_t* ridx;           // [S][T][R]
+  float* rwt;
+  int32_t S, H, T, d_k, n_sub, W, R;
+};
+
+hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream);
+
+struct GdnArgs {
+  float* S;                // [S][d_v][d_k]
+  const void* k;           // [S][T][d_k]
+  const void* q;
+  const void* v;           // [S][T][d_v]
+  const float* alpha;
+  const float* beta;
+  float* out;              // [S][T][d_v]
+  int32_t nS, T, d_k, d_v;
+};
+
+hipError_t launch_gdn(const GdnArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace sdm

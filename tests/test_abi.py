@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_addressed_linear_amd as sdm
+    if not os.path.exists(sdm.LIB_PATH):
+        pytest.skip("libsdm.so not built")
+    return sdm.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(
+        ["sdm_score_topk", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
+         "sdm_status_str", "sdm_version"])
+
+
+def test_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.sdm_version().decode().count(".") == 2
+    for code in range(8):
+        assert L.sdm_status_str(code)
+    assert L.sdm_status_str(99) == b"unknown status"
+
+
+def dims(**kw):
+    import sparse_addressed_linear_amd as sdm
+    base = dict(B=1, H=1, T=4, d_k=32, n_sub=32, d_v=16, W=8, R=8)
+    base.update(kw)
+    return sdm.Dims(**base)
+
+
+P = ctypes.c_void_p(4096)  # aligned, never dereferenced: validation fails first
+
+
+def score(L, d, dt=1, ptr=P, null_at=None):
+    args = [ptr] * 7
+    if null_at is not None:
+        args[null_at] = ctypes.c_void_p(0)
+    return L.sdm_score_topk(ctypes.byref(d), dt, *args, None)
+
+
+def test_score_topk_rejects(L):
+    for i in range(7):
+        assert score(L, dims(), null_at=i) == 1
+    assert L.sdm_score_topk(None, 1, *([P] * 7), None) == 1
+    assert score(L, dims(d_k=31)) == 2          # odd d_k
+    assert score(L, dims(W=0)) == 2
+    assert score(L, dims(W=1025)) == 2          # W > N
+    assert score(L, dims(n_sub=50000)) == 2     # N >= 2^31
+    assert score(L, dims(), dt=7) == 3
+    assert score(L, dims(n_sub=2048, W=8)) == 4  # kernel limits
+    assert score(L, dims(d_k=40)) == 4          # half not a multiple of 16
+    assert score(L, dims(W=33)) == 4            # W > n_sub
+    assert score(L, dims(n_sub=256, W=129, R=8)) == 4
+    assert score(L, dims(), ptr=ctypes.c_void_p(4100)) == 5
+
+
+def scan(L, d, dt=0, ptr=P, ws=0, null_at=None):
+    args = [ptr] * 9
+    if null_at is not None:
+        args[null_at] = ctypes.c_void_p(0)
+    return L.sdm_scan(ctypes.byref(d), dt, *args, ptr, ctypes.c_size_t(ws), None)
+
+
+def test_empty_sequence_accepts_null_token_tensors(L):
+    z = ctypes.c_void_p(0)
+    d = dims(T=0)
+    assert L.sdm_score_topk(ctypes.byref(d), 1, z, z, P, z, z, z, z, None) == 0
+    assert L.sdm_scan(ctypes.byref(d), 0, P, *([z] * 8), z, ctypes.c_size_t(0), None) == 0
+    assert L.sdm_gdn_scan(1, 1, 0, 128, 128, 0, P, *([z] * 6), None) == 0
+    assert L.sdm_scan(ctypes.byref(d), 0, z, *([z] * 8), z, ctypes.c_size_t(0), None) == 1
+
+
+def test_scan_rejects(L):
+    for i in range(9):
+        assert scan(L, dims(), null_at=i) == 1
+    assert scan(L, dims(R=0)) == 2
+    assert scan(L, dims(), dt=5) == 3
+    assert scan(L, dims(d_v=20)) == 4
+    assert scan(L, dims(n_sub=64, W=300)) == 4
+    assert scan(L, dims(), ptr=ctypes.c_void_p(4104)) == 5
+
+
+def test_scan_workspace_contract(L):
+    import sparse_addressed_linear_amd as sdm
+    # a large multi-stream problem spreads each stream over slot partitions
+    d = dims(B=8, H=8, T=4096, d_k=128, n_sub=1024, d_v=64, W=64, R=64)
+    need = L.sdm_scan_workspace_size(ctypes.byref(d))
+    assert need > 0 and need % (8 * 8 * 4096 * 64 * 4) == 0
+    assert scan(L, d, ws=need - 1) == 7
+    assert sdm.scan_workspace_size(8, 8, 4096, 1 << 20, 64, 64, 64) == need
+    assert L.sdm_scan_workspace_size(ctypes.byref(dims(W=0))) == 0
+
+
+def test_gdn_rejects(L):
+    args = [P] * 7
+    assert L.sdm_gdn_scan(1, 1, 4, 128, 128, 0, ctypes.c_void_p(0), *args[1:], None) == 1
+    assert L.sdm_gdn_scan(0, 1, 4, 128, 128, 0, *args, None) == 2
+    assert L.sdm_gdn_scan(1, 1, 4, 128, 128, 9, *args, None) == 3
+    assert L.sdm_gdn_scan(1, 1, 4, 64, 128, 0, *args, None) == 4
+    assert L.sdm_gdn_scan(1, 1, 4, 128, 128, 0, ctypes.c_void_p(4097), *args[1:], None) == 5
+
+
+def test_python_binding_requires_device_tensors():
+    import torch
+    import sparse_addressed_linear_amd as sdm
+    if not os.path.exists(sdm.LIB_PATH):
+        pytest.skip("libsdm.so not built")
+    x = torch.zeros(1, 1, 4, 32)
+    C = torch.zeros(1, 2, 32, 16)
+    with pytest.raises(ValueError, match="device tensor"):
+        sdm.score_topk(x, x, C, 8, 8)
