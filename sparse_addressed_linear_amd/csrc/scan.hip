@@ -268,19 +268,15 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 
     if (!ovf) {
-      // ---- 5. level 0 from the speculative loads --------------------------
+      // ---- 5. level-0 writes from the speculative loads -------------------
 #pragma unroll
       for (int i = 0; i < kEPL; i++) {
         const int e = i * GPW + g;
-        if (e < ne && (mymeta[e] & 0xff) == 0) {
-          if (e < nw) {
-            float c, omc;
-            gate(beta, mywt[e], c, omc);
-            *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
-                upd4(x[i], alpha, omc, c, vv);
-          } else {
-            acc = fma4(mywt[e], x[i], acc);
-          }
+        if (e < nw && (mymeta[e] & 0xff) == 0) {
+          float c, omc;
+          gate(beta, mywt[e], c, omc);
+          *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
+              upd4(x[i], alpha, omc, c, vv);
         }
       }
       __syncthreads();  // BAR_A: level-0 stores before level-1 loads; max level known
@@ -296,18 +292,21 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
 #pragma unroll
         for (int i = 0; i < kEPL; i++) {
           const int e = i * GPW + g;
-          if (e < ne && (mymeta[e] & 0xff) == L) {
-            if (e < nw) {
-              float c, omc;
-              gate(beta, mywt[e], c, omc);
-              *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
-                  upd4(x[i], alpha, omc, c, vv);
-            } else {
-              acc = fma4(mywt[e], x[i], acc);
-            }
+          if (e < nw && (mymeta[e] & 0xff) == L) {
+            float c, omc;
+            gate(beta, mywt[e], c, omc);
+            *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
+                upd4(x[i], alpha, omc, c, vv);
           }
         }
         __syncthreads();  // level-L stores before level-(L+1) loads
+      }
+      // every read row now holds the value its token must see: sum them in
+      // event order, so the result does not depend on where blocks start
+#pragma unroll
+      for (int i = 0; i < kEPL; i++) {
+        const int e = i * GPW + g;
+        if (e >= nw && e < ne) acc = fma4(mywt[e], x[i], acc);
       }
     } else {
       // ---- overflow path: some token has more events than fit in registers.
