@@ -11,29 +11,44 @@
 // GPU decomposition (all exact, because rows and columns evolve independently):
 //   - stream          : one (b,h) table, N rows of d_v fp32.
 //   - column slice    : CW = 4*LPR consecutive columns (>= 64 B per row access).
-//   - slot partition  : rows with slot & (P-1) == p.  A token's events are split
-//                       across the P partitions; each partition workgroup
+//   - slot partition  : rows whose slot hash falls in partition p (a hash, not
+//                       slot bits: product-key slots of one token share
+//                       sub-key indices, so their low bits are far from
+//                       uniform).  A token's events are split across the P
+//                       partitions; each partition workgroup
 //                       produces a partial read sum, added in partition order
 //                       by sdm_partial_sum_kernel.
 // One workgroup owns one (stream, slice, partition) and walks all tokens.
 //
-// Inside a workgroup, tokens are processed in blocks of NW tokens, one wave
-// per token.  All row loads of a block are issued before any row of the block
-// is stored, so every event sees the state before the block, unless the block
-// itself wrote its slot earlier.  Such in-block dependences are found with an
-// LDS hash of the block's write slots (slot -> bitmask of writing tokens):
-//   write at token u of slot s : level = #{in-block writers of s before u}
-//   read  at token u of slot s : level = #{in-block writers of s at or before u}
-// Level-0 events use the speculative loads; level-L events reload after the
-// level-(L-1) stores (barrier), and within a level all loads precede all stores
-// (a level-L read of s must not see the level-L write of s by a later token).
-// Writes of one slot get distinct levels, so a level never races with itself.
+// Inside a workgroup, tokens go in blocks of NW tokens, one wave per token.
+// Block b's rows are loaded during block b-1, right after block b-1's last
+// stores (a barrier orders them), so every load sees the state before block
+// b; their latency overlaps block b's own set-up (hash build, dependence
+// levels, two barriers), which issues no memory operation.  The indices of
+// block b+1 are prefetched one block earlier still.  In-block dependences
+// come from an LDS hash of the block's write slots (slot -> bitmask of
+// writing tokens):
+//   write at token u of slot s : level = #{block writers of s before u}
+//   read  at token u of slot s : level = #{block writers of s at or before u}
+// Level-0 events use the loaded rows; level-L events (L >= 1) reload after
+// the level-(L-1) stores (barrier), and all loads of a level come before its
+// stores (a level-L read of s must not see the level-L write of s by a later
+// token).  Writes of one slot get distinct levels, so a level never races
+// with itself.  Reads are summed after all levels in fixed event order, so
+// the output does not depend on where blocks start.
+//
+// Memory operations on the common path are unconditional (clamped or dummy
+// addresses) and issued oldest-needed first, so the compiler's in-order wait
+// counts are exact and never drain loads that are still meant to be in
+// flight.
 //
 // gfx950 workgroup memory ordering: all waves of a workgroup share the CU's
 // in-order vector L1, and __syncthreads() (workgroup-scope release/acquire)
 // orders a wave's earlier global stores before another wave's later global
-// loads, without draining the stores.
+// loads, without draining the stores.  A load issued before a barrier cannot
+// see a store issued after it.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "sdm_internal.h"
@@ -42,7 +57,8 @@ namespace sdm {
 
 namespace {
 
-constexpr int kEPL = 16;  // events per lane group kept in flight (registers)
+constexpr int kLevel = 0x7f;
+constexpr uint64_t kEmpty = 0x00000000ffffffffull;  // hash entry: key -1, no writers
 
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
@@ -66,21 +82,21 @@ __device__ __forceinline__ float4 load_v4(const void* v, bool bf16, int64_t off)
   return *reinterpret_cast<const float4*>(static_cast<const float*>(v) + off);
 }
 
-// Gated delta update of one float4 of a row: (1-c)*(a*m) + c*v, each operation
-// rounded separately (no contraction), so c == 1 gives v and c == 0 gives a*m.
+// write strength c = beta*w and 1 - c, each rounded separately
+__device__ __forceinline__ void gate(float beta, float w, float& c, float& omc) {
+#pragma clang fp contract(off)
+  c = beta * w;
+  omc = 1.0f - c;
+}
+
+// Gated delta update of one element: (1-c)*(a*m) + c*v, each product and the
+// sum rounded separately (no contraction), so c == 1 gives v, c == 0 gives a*m.
 __device__ __forceinline__ float upd(float m, float a, float omc, float c, float v) {
 #pragma clang fp contract(off)
   const float mt = a * m;
   const float keep = omc * mt;
   const float put = c * v;
   return keep + put;
-}
-
-// write strength c = beta*w and 1 - c, each rounded separately
-__device__ __forceinline__ void gate(float beta, float w, float& c, float& omc) {
-#pragma clang fp contract(off)
-  c = beta * w;
-  omc = 1.0f - c;
 }
 
 __device__ __forceinline__ float4 upd4(float4 m, float a, float omc, float c, float4 v) {
@@ -102,26 +118,39 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// writer mask of slot s in table h (0 when absent)
+__device__ __forceinline__ uint32_t probe(const uint64_t* h, int hmsk, int32_t s) {
+  int p = (int)(mix32((uint32_t)s) & (uint32_t)hmsk);
+  while (true) {
+    const uint64_t ent = h[p];
+    const int32_t k = (int32_t)(uint32_t)ent;
+    if (k == s) return (uint32_t)(ent >> 32);
+    if (k == -1) return 0u;
+    p = (p + 1) & hmsk;
+  }
+}
+
 }  // namespace
 
 // LPR: lanes per row slice (CW = 4*LPR columns).  NW: waves = tokens per block.
-template <int LPR, bool VBF16, int NW>
+// MC: 64-wide chunks of a token's index list (W, R <= 64*MC).  EPL: events per
+// lane group held in registers (a wave holds EPL*64/LPR events).
+template <int LPR, bool VBF16, int NW, int MC, int EPL>
 __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
-  constexpr int GPW = 64 / LPR;   // lane groups per wave
-  constexpr int CAPW = GPW * kEPL;  // events per wave held in registers
+  constexpr int GPW = 64 / LPR;    // lane groups per wave
+  constexpr int CAPW = GPW * EPL;  // events per wave held in registers
   constexpr int CW = 4 * LPR;
+  constexpr int NT = NW * 64;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  int32_t* hkey = reinterpret_cast<int32_t*>(smem);          // [2][hsize]
-  uint32_t* hmask = reinterpret_cast<uint32_t*>(hkey + 2 * a.hsize);
-  int32_t* lslot = reinterpret_cast<int32_t*>(hmask + 2 * a.hsize);  // [NW][lcap]
-  float* lwt = reinterpret_cast<float*>(lslot + NW * a.lcap);
-  int32_t* lmeta = reinterpret_cast<int32_t*>(lwt + NW * a.lcap);    // level | hpos<<8
-  __shared__ int s_maxlvl[2];
-  __shared__ int s_ovf[2];
+  uint64_t* htab = reinterpret_cast<uint64_t*>(smem);              // [hsize]
+  int32_t* lslot = reinterpret_cast<int32_t*>(htab + a.hsize);     // [NW][lcap]
+  float* lwt = reinterpret_cast<float*>(lslot + NW * a.lcap);      // [NW][lcap]
+  int32_t* lmeta = reinterpret_cast<int32_t*>(lwt + NW * a.lcap);  // [NW][lcap]
+  __shared__ int s_flag[3][2];  // per block (index mod 3): max level, overflow
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int g = lane / LPR;  // lane group within the wave
   const int l = lane % LPR;  // float4 index within the row slice
@@ -140,163 +169,190 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
   const int pp = sub / a.CS;
   const int c0 = cs * CW + 4 * l;  // this lane's first column
   const uint32_t pmask = (uint32_t)a.P - 1u;
-
-  float* Mst = a.M + (int64_t)st * a.N * a.d_v + c0;
+  const int nblk = (a.T + NW - 1) / NW;
   const int hmsk = a.hsize - 1;
+  float* Mst = a.M + (int64_t)st * a.N * a.d_v + c0;
+  int32_t* sl = lslot + wave * a.lcap;  // this wave's event list
+  float* wl = lwt + wave * a.lcap;
+  int32_t* ml = lmeta + wave * a.lcap;
 
-  int32_t* myslot = lslot + wave * a.lcap;
-  float* mywt = lwt + wave * a.lcap;
-  int32_t* mymeta = lmeta + wave * a.lcap;
+  auto row = [&](int32_t s) -> float* { return Mst + (int64_t)s * a.d_v; };
+  auto in_part = [&](int32_t s) { return ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp; };
 
-  // initialise both hash tables and flags
-  for (int i = tid; i < 2 * a.hsize; i += NW * 64) hkey[i] = -1, hmask[i] = 0u;
-  if (tid < 2) s_maxlvl[tid] = 0, s_ovf[tid] = 0;
-  __syncthreads();
-
-  for (int t0 = 0, blk = 0; t0 < a.T; t0 += NW, blk++) {
-    const int hb = blk & 1;
-    int32_t* hk = hkey + hb * a.hsize;
-    uint32_t* hm = hmask + hb * a.hsize;
-    const int tok = t0 + wave;
-    const bool valid = tok < a.T;
-    const int64_t trow = (int64_t)st * a.T + tok;  // token row in [S][T]
-
-    // ---- 1. compact this partition's events of the wave's token ----------
-    int nw = 0, nr = 0;
-    if (valid) {
-      const int32_t* wi = a.widx + trow * a.W;
-      const float* ww = a.wwt + trow * a.W;
-      for (int c = 0; c < a.W; c += 64) {
-        const int i = c + lane;
-        int32_t s = -1;
-        float w = 0.f;
-        if (i < a.W) s = wi[i], w = ww[i];
-        const bool f = s >= 0 && (((uint32_t)s & pmask) == (uint32_t)pp);
+  // ---- index prefetch for one token (registers; unconditional loads) -----
+  int32_t ps[MC], qs[MC];
+  float pw[MC], qw[MC];
+  bool pok = false;  // the prefetched token exists
+  auto prefetch = [&](int blk) {
+    const int tok = blk * NW + wave;
+    pok = blk < nblk && tok < a.T;
+    const int64_t trow = (int64_t)st * a.T + (pok ? tok : 0);
+#pragma unroll
+    for (int c = 0; c < MC; c++) {
+      const int i = c * 64 + lane;
+      const int iw = i < a.W ? i : a.W - 1, ir = i < a.R ? i : a.R - 1;
+      ps[c] = a.widx[trow * a.W + iw];
+      pw[c] = a.wwt[trow * a.W + iw];
+      qs[c] = a.ridx[trow * a.R + ir];
+      qw[c] = a.rwt[trow * a.R + ir];
+    }
+  };
+  // the prefetched token's events of this partition into the wave's list:
+  // writes first, then reads, each in rank order
+  auto compact = [&](int& nw, int& nr) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    nw = 0;
+#pragma unroll
+    for (int c = 0; c < MC; c++) {
+      if (c * 64 < a.W) {
+        const bool f = pok && c * 64 + lane < a.W && in_part(ps[c]);
         const uint64_t bal = __ballot(f);
         if (f) {
-          const int pos = nw + __popcll(bal & ((1ull << lane) - 1ull));
-          myslot[pos] = s;
-          mywt[pos] = w;
+          const int pos = nw + __popcll(bal & below);
+          sl[pos] = ps[c];
+          wl[pos] = pw[c];
         }
         nw += __popcll(bal);
       }
-      const int32_t* ri = a.ridx + trow * a.R;
-      const float* rw = a.rwt + trow * a.R;
-      for (int c = 0; c < a.R; c += 64) {
-        const int i = c + lane;
-        int32_t s = -1;
-        float w = 0.f;
-        if (i < a.R) s = ri[i], w = rw[i];
-        const bool f = s >= 0 && (((uint32_t)s & pmask) == (uint32_t)pp);
+    }
+    nr = 0;
+#pragma unroll
+    for (int c = 0; c < MC; c++) {
+      if (c * 64 < a.R) {
+        const bool f = pok && c * 64 + lane < a.R && in_part(qs[c]);
         const uint64_t bal = __ballot(f);
         if (f) {
-          const int pos = nw + nr + __popcll(bal & ((1ull << lane) - 1ull));
-          myslot[pos] = s;
-          mywt[pos] = w;
+          const int pos = nw + nr + __popcll(bal & below);
+          sl[pos] = qs[c];
+          wl[pos] = qw[c];
         }
         nr += __popcll(bal);
       }
     }
-    const int ne = nw + nr;
-    const bool fits = ne <= CAPW;
-    wave_lds_sync();  // list entries written by other lanes are read below
-
-    // ---- 2. speculative loads of every event row (state before the block) --
-    float4 x[kEPL];
-    if (fits) {
+  };
+  // gates and this lane's slice of v for the wave's token of block blk
+  // (clamped, always loaded)
+  auto gates = [&](int blk, float& al, float& be, float4& vv) {
+    const int tok = blk * NW + wave;
+    const int64_t tr = (int64_t)st * a.T + (tok < a.T ? tok : 0);
+    al = a.alpha[tr];
+    be = a.beta[tr];
+    vv = load_v4(a.v, VBF16, tr * a.d_v + c0);
+  };
+  // every lane always issues EPL row loads; positions past the list read row
+  // 0 of the stream (one cache line per instruction, never used)
+  auto issue = [&](int ne, float4(&x)[EPL]) {
 #pragma unroll
-      for (int i = 0; i < kEPL; i++) {
-        const int e = i * GPW + g;
-        if (e < ne) x[i] = *reinterpret_cast<const float4*>(Mst + (int64_t)myslot[e] * a.d_v);
-      }
+    for (int i = 0; i < EPL; i++) {
+      const int e = i * GPW + g;
+      x[i] = *reinterpret_cast<const float4*>(row(e < ne ? sl[e] : 0));
     }
+  };
 
-    // ---- 3. insert write slots into this block's hash ---------------------
-    for (int e = lane; e < nw; e += 64) {
-      const int32_t s = myslot[e];
-      int h = (int)(mix32((uint32_t)s) & (uint32_t)hmsk);
+  // ---- set-up: empty hash, clear flags, block 0 in flight ----------------
+  for (int i = tid; i < a.hsize; i += NT) htab[i] = kEmpty;
+  if (tid < 6) s_flag[tid / 2][tid % 2] = 0;
+  __syncthreads();
+  float4 X[EPL];
+  int nwc = 0, nrc = 0;
+  float gA, gB;
+  float4 gV;
+  prefetch(0);
+  compact(nwc, nrc);
+  wave_lds_sync();
+  gates(0, gA, gB, gV);
+  prefetch(1);
+  {
+    const bool fit = nwc + nrc <= CAPW;
+    issue(fit ? nwc + nrc : 0, X);
+    if (!fit && lane == 0) atomicOr(&s_flag[0][1], 1);
+  }
+
+  for (int b = 0; b < nblk; b++) {
+    const int fcur = b % 3, fnext = (b + 1) % 3, fprev = (b + 2) % 3;
+    const int tok = b * NW + wave;
+    const bool valid = tok < a.T;
+    const int64_t trow = (int64_t)st * a.T + tok;
+    const int nec = nwc + nrc;
+    const float alpha = gA, beta = gB;
+    const float4 vv = gV;
+
+    // ---- 1. block b's writers into the hash ------------------------------
+    for (int e = lane; e < nwc; e += 64) {
+      const int32_t s = sl[e];
+      const uint64_t mine = (uint64_t)(uint32_t)s | ((uint64_t)(1u << wave) << 32);
+      int p = (int)(mix32((uint32_t)s) & (uint32_t)hmsk);
       while (true) {
-        const int32_t old = atomicCAS(&hk[h], -1, s);
-        if (old == -1 || old == s) break;
-        h = (h + 1) & hmsk;
-      }
-      atomicOr(&hm[h], 1u << wave);
-      mymeta[e] = h << 8;
-    }
-    if (!fits && lane == 0) atomicOr(&s_ovf[hb], 1);
-    // gates and this lane's slice of v for the wave's token
-    float alpha = 0.f, beta = 0.f;
-    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (valid) {
-      alpha = a.alpha[trow];
-      beta = a.beta[trow];
-      vv = load_v4(a.v, VBF16, trow * a.d_v + c0);
-    }
-    __syncthreads();  // BAR1: all inserts visible; all speculative loads issued
-
-    // the previous block's flags are no longer read by anyone: reset them
-    if (tid == 0) s_maxlvl[hb ^ 1] = 0, s_ovf[hb ^ 1] = 0;
-
-    // ---- 4. dependence levels ---------------------------------------------
-    int mylvl = 0;
-    const uint32_t wbefore = (1u << wave) - 1u;   // writers strictly before
-    const uint32_t rbefore = (2u << wave) - 1u;   // writers at or before
-    for (int e = lane; e < ne; e += 64) {
-      const int32_t s = myslot[e];
-      int h = (int)(mix32((uint32_t)s) & (uint32_t)hmsk);
-      uint32_t m = 0u;
-      while (true) {
-        const int32_t k = hk[h];
-        if (k == s) {
-          m = hm[h];
+        const uint64_t old = atomicCAS(reinterpret_cast<unsigned long long*>(&htab[p]),
+                                       (unsigned long long)kEmpty, (unsigned long long)mine);
+        if (old == kEmpty) break;
+        if ((int32_t)(uint32_t)old == s) {
+          atomicOr(reinterpret_cast<unsigned long long*>(&htab[p]),
+                   (unsigned long long)((uint64_t)(1u << wave) << 32));
           break;
         }
-        if (k == -1) break;
-        h = (h + 1) & hmsk;
+        p = (p + 1) & hmsk;
       }
-      const int lvl = __popc(m & (e < nw ? wbefore : rbefore));
-      if (e < nw) mymeta[e] |= lvl;
-      else mymeta[e] = lvl;
+    }
+    __syncthreads();  // BAR1: block b's hash complete
+    if (tid == 0) s_flag[fprev][0] = 0, s_flag[fprev][1] = 0;  // block b-1's flags
+
+    // ---- 2. dependence levels --------------------------------------------
+    int mylvl = 0;
+    const uint32_t wbefore = (1u << wave) - 1u;  // writers strictly before
+    const uint32_t rbefore = (2u << wave) - 1u;  // writers at or before
+    for (int e = lane; e < nec; e += 64) {
+      const uint32_t m = probe(htab, hmsk, sl[e]);
+      const int lvl = __popc(m & (e < nwc ? wbefore : rbefore));
+      ml[e] = lvl;
       mylvl = max(mylvl, lvl);
     }
     wave_lds_sync();  // levels written by other lanes are read below
-    // wave max then workgroup max
     for (int o = 32; o > 0; o >>= 1) mylvl = max(mylvl, __shfl_xor(mylvl, o));
-    if (lane == 0 && mylvl > 0) atomicMax(&s_maxlvl[hb], mylvl);
-    const bool ovf = s_ovf[hb] != 0;  // set before BAR1
+    if (lane == 0 && mylvl > 0) atomicMax(&s_flag[fcur][0], mylvl);
+    __syncthreads();  // BAR2: levels of block b complete
+    const int maxL = s_flag[fcur][0];
+    const bool ovf = s_flag[fcur][1] != 0;
 
+    // ---- 3. level 0 (and, without dependences, the reads) -----------------
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-
     if (!ovf) {
-      // ---- 5. level-0 writes from the speculative loads -------------------
 #pragma unroll
-      for (int i = 0; i < kEPL; i++) {
+      for (int i = 0; i < EPL; i++) {
         const int e = i * GPW + g;
-        if (e < nw && (mymeta[e] & 0xff) == 0) {
+        if (e < nwc && (ml[e] & kLevel) == 0) {
           float c, omc;
-          gate(beta, mywt[e], c, omc);
-          *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
-              upd4(x[i], alpha, omc, c, vv);
+          gate(beta, wl[e], c, omc);
+          *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
         }
       }
-      __syncthreads();  // BAR_A: level-0 stores before level-1 loads; max level known
-      const int maxL = s_maxlvl[hb];
+      if (maxL == 0) {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+          const int e = i * GPW + g;
+          if (e >= nwc && e < nec) acc = fma4(wl[e], X[i], acc);
+        }
+      }
+    }
+    for (int i = tid; i < a.hsize; i += NT) htab[i] = kEmpty;  // lookups are done
+    __syncthreads();  // BAR_A: level-0 stores before any later load
+
+    // ---- 4. dependent levels ---------------------------------------------
+    if (!ovf && maxL > 0) {
       for (int L = 1; L <= maxL; L++) {
 #pragma unroll
-        for (int i = 0; i < kEPL; i++) {
+        for (int i = 0; i < EPL; i++) {
           const int e = i * GPW + g;
-          if (e < ne && (mymeta[e] & 0xff) == L)
-            x[i] = *reinterpret_cast<const float4*>(Mst + (int64_t)myslot[e] * a.d_v);
+          if (e < nec && (ml[e] & kLevel) == L) X[i] = *reinterpret_cast<const float4*>(row(sl[e]));
         }
         __syncthreads();  // every level-L load issued before any level-L store
 #pragma unroll
-        for (int i = 0; i < kEPL; i++) {
+        for (int i = 0; i < EPL; i++) {
           const int e = i * GPW + g;
-          if (e < nw && (mymeta[e] & 0xff) == L) {
+          if (e < nwc && (ml[e] & kLevel) == L) {
             float c, omc;
-            gate(beta, mywt[e], c, omc);
-            *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
-                upd4(x[i], alpha, omc, c, vv);
+            gate(beta, wl[e], c, omc);
+            *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
           }
         }
         __syncthreads();  // level-L stores before level-(L+1) loads
@@ -304,46 +360,41 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
       // every read row now holds the value its token must see: sum them in
       // event order, so the result does not depend on where blocks start
 #pragma unroll
-      for (int i = 0; i < kEPL; i++) {
+      for (int i = 0; i < EPL; i++) {
         const int e = i * GPW + g;
-        if (e >= nw && e < ne) acc = fma4(mywt[e], x[i], acc);
+        if (e >= nwc && e < nec) acc = fma4(wl[e], X[i], acc);
       }
-    } else {
-      // ---- overflow path: some token has more events than fit in registers.
-      // Per level: all reads (chunked, no stores), barrier, all writes
-      // (chunked; writes of one level never share a slot), barrier.
-      __syncthreads();  // max level known
-      const int maxL = s_maxlvl[hb];
+    } else if (ovf) {
+      // overflow path: some token has more events than fit in registers.  Per
+      // level: all reads (chunked, no stores), barrier, all writes (chunked;
+      // writes of one level never share a slot), barrier.
       for (int L = 0; L <= maxL; L++) {
-        for (int base = nw; base < ne; base += CAPW) {
+        for (int base = nwc; base < nec; base += CAPW) {
 #pragma unroll
-          for (int i = 0; i < kEPL; i++) {
+          for (int i = 0; i < EPL; i++) {
             const int e = base + i * GPW + g;
-            if (e < ne && (mymeta[e] & 0xff) == L)
-              x[i] = *reinterpret_cast<const float4*>(Mst + (int64_t)myslot[e] * a.d_v);
+            if (e < nec && (ml[e] & kLevel) == L) X[i] = *reinterpret_cast<const float4*>(row(sl[e]));
           }
 #pragma unroll
-          for (int i = 0; i < kEPL; i++) {
+          for (int i = 0; i < EPL; i++) {
             const int e = base + i * GPW + g;
-            if (e < ne && (mymeta[e] & 0xff) == L) acc = fma4(mywt[e], x[i], acc);
+            if (e < nec && (ml[e] & kLevel) == L) acc = fma4(wl[e], X[i], acc);
           }
         }
         __syncthreads();  // level-L reads done before level-L writes store
-        for (int base = 0; base < nw; base += CAPW) {
+        for (int base = 0; base < nwc; base += CAPW) {
 #pragma unroll
-          for (int i = 0; i < kEPL; i++) {
+          for (int i = 0; i < EPL; i++) {
             const int e = base + i * GPW + g;
-            if (e < nw && (mymeta[e] & 0xff) == L)
-              x[i] = *reinterpret_cast<const float4*>(Mst + (int64_t)myslot[e] * a.d_v);
+            if (e < nwc && (ml[e] & kLevel) == L) X[i] = *reinterpret_cast<const float4*>(row(sl[e]));
           }
 #pragma unroll
-          for (int i = 0; i < kEPL; i++) {
+          for (int i = 0; i < EPL; i++) {
             const int e = base + i * GPW + g;
-            if (e < nw && (mymeta[e] & 0xff) == L) {
+            if (e < nwc && (ml[e] & kLevel) == L) {
               float c, omc;
-              gate(beta, mywt[e], c, omc);
-              *reinterpret_cast<float4*>(Mst + (int64_t)myslot[e] * a.d_v) =
-                  upd4(x[i], alpha, omc, c, vv);
+              gate(beta, wl[e], c, omc);
+              *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
             }
           }
         }
@@ -351,7 +402,7 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
       }
     }
 
-    // ---- 6. read sum across the wave's lane groups (fixed order) ----------
+    // ---- 5. read sum across the wave's lane groups (fixed order) ----------
 #pragma unroll
     for (int o = LPR; o < 64; o <<= 1) acc = add4(acc, shfl_xor4(acc, o));
     if (valid && g == 0) {
@@ -360,12 +411,19 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
       *reinterpret_cast<float4*>(dst) = acc;
     }
 
-    // ---- 7. clear this block's hash entries (all lookups are done) --------
-    for (int e = lane; e < nw; e += 64) {
-      const int h = mymeta[e] >> 8;
-      hk[h] = -1;
-      hm[h] = 0u;
-    }
+    // ---- 6. next block: compact, gates, indices after it, then its rows ---
+    // (every store of block b precedes these loads: the last barrier above
+    // follows the last store)
+    int nwn = 0, nrn = 0;
+    if (b + 1 < nblk) compact(nwn, nrn);
+    wave_lds_sync();
+    gates(b + 1, gA, gB, gV);
+    prefetch(b + 2);
+    const bool fit = nwn + nrn <= CAPW;
+    issue(fit ? nwn + nrn : 0, X);
+    if (b + 1 < nblk && !fit && lane == 0) atomicOr(&s_flag[fnext][1], 1);
+    nwc = nwn;
+    nrc = nrn;
   }
 }
 
@@ -383,9 +441,9 @@ __global__ void __launch_bounds__(256) sdm_partial_sum_kernel(const float* __res
 
 // ----------------------------------------------------------------- launch --
 
-template <int LPR, bool VBF16, int NW>
+template <int LPR, bool VBF16, int NW, int MC, int EPL>
 static hipError_t launch_scan_t(const ScanArgs& a, size_t lds, hipStream_t stream) {
-  auto k = sdm_scan_kernel<LPR, VBF16, NW>;
+  auto k = sdm_scan_kernel<LPR, VBF16, NW, MC, EPL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -405,11 +463,18 @@ ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R) {
          (W + R) / (P * 2) >= 16 && P * 2 <= N)
     P *= 2;
   p.P = P;
+  // registers per lane group: the mean events of a token in one partition
+  // plus four standard deviations (partitions are hashed, so the count is
+  // close to binomial); rarer tokens take the overflow path
+  const double mean = (double)(W + R) / P;
+  const double need = mean + 4.0 * sqrt(mean * (1.0 - 1.0 / P)) + 1.0;
+  const int gpw = 64 / p.lpr;
+  p.epl = need <= 8 * gpw ? 8 : (need <= 12 * gpw ? 12 : 16);
   int64_t hs = 1;
   while (hs < 2LL * p.nw * W) hs *= 2;
   p.hsize = (int)hs;
   p.lcap = W + R;
-  p.lds = (size_t)2 * p.hsize * 8 + (size_t)p.nw * p.lcap * 12;
+  p.lds = (size_t)p.hsize * 8 + (size_t)p.nw * p.lcap * 12;
   p.work_bytes = P > 1 ? (size_t)P * S * T * d_v * sizeof(float) : 0;
   return p;
 }
@@ -423,13 +488,21 @@ hipError_t launch_scan(const ScanArgs& a0, const ScanPlan& p, bool vbf16, hipStr
   a.xcd_map = ((int64_t)a.S * a.CS * a.P) % 8 == 0 ? 1 : 0;
   if (a.T == 0) return hipSuccess;
   hipError_t e;
-#define SDM_SCAN_CASE(LPR_, NW_)                                                 \
-  if (p.lpr == LPR_ && p.nw == NW_) {                                            \
-    e = vbf16 ? launch_scan_t<LPR_, true, NW_>(a, p.lds, stream)                 \
-              : launch_scan_t<LPR_, false, NW_>(a, p.lds, stream);               \
+  const int mc = (a.W > a.R ? a.W : a.R) <= 64 ? 1 : ((a.W > a.R ? a.W : a.R) <= 128 ? 2 : 4);
+#define SDM_SCAN_CASE(LPR_, MC_, EPL_)                                           \
+  if (p.lpr == LPR_ && mc == MC_ && p.epl == EPL_) {                             \
+    e = vbf16 ? launch_scan_t<LPR_, true, 8, MC_, EPL_>(a, p.lds, stream)        \
+              : launch_scan_t<LPR_, false, 8, MC_, EPL_>(a, p.lds, stream);      \
   } else
-  SDM_SCAN_CASE(8, 8)
-  SDM_SCAN_CASE(4, 8) { return hipErrorInvalidValue; }
+#define SDM_SCAN_EPL(LPR_, MC_) \
+  SDM_SCAN_CASE(LPR_, MC_, 8) SDM_SCAN_CASE(LPR_, MC_, 12) SDM_SCAN_CASE(LPR_, MC_, 16)
+  SDM_SCAN_EPL(8, 1)
+  SDM_SCAN_EPL(8, 2)
+  SDM_SCAN_EPL(8, 4)
+  SDM_SCAN_EPL(4, 1)
+  SDM_SCAN_EPL(4, 2)
+  SDM_SCAN_EPL(4, 4) { return hipErrorInvalidValue; }
+#undef SDM_SCAN_EPL
 #undef SDM_SCAN_CASE
   if (e != hipSuccess) return e;
   if (p.P > 1) {

@@ -39,6 +39,7 @@ struct ScanPlan {
   int CS;       // column slices per stream
   int P;        // slot partitions
   int nw;       // waves per workgroup = tokens per block
+  int epl;      // row slices per lane group held in registers
   int hsize;    // LDS hash size (power of two)
   int lcap;     // per-wave event list capacity
   size_t lds;   // dynamic LDS bytes
