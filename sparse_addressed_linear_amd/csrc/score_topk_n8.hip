@@ -1,0 +1,6 @@
+// Instances of the product-key addressing kernel with 8 stage-1 score(s) per lane.
+#include "score_topk_impl.h"
+
+namespace sdm {
+template hipError_t launch_score_n<8>(const ScoreArgs&, bool, int, hipStream_t);
+}  // namespace sdm
