@@ -41,10 +41,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTT = 16;      // tokens per workgroup
+constexpr int kTT = 8;       // tokens per workgroup (MFMA tiles carry 16 columns)
 constexpr int kWaves = 8;    // waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kCapMax = 512; // largest candidate set sorted at once
+constexpr int kCapMax = 256; // largest candidate set sorted at once
 constexpr int kGridMax = 1024;  // largest pruned grid held in registers
 
 __device__ __forceinline__ uint32_t ord32(float s) {
@@ -174,8 +174,7 @@ template <typename Emit>
 __device__ __forceinline__ void sort_emit(uint64_t* buf, int c, int k, int lane, Emit emit) {
   if (c <= 64) sort_emit_e<1>(buf, c, k, lane, emit);
   else if (c <= 128) sort_emit_e<2>(buf, c, k, lane, emit);
-  else if (c <= 256) sort_emit_e<4>(buf, c, k, lane, emit);
-  else sort_emit_e<8>(buf, c, k, lane, emit);
+  else sort_emit_e<4>(buf, c, k, lane, emit);
 }
 
 // Compact keys >= t into buf (ballot order); returns the count.
@@ -226,7 +225,7 @@ __host__ __device__ inline ScoreSmem score_smem(int n_sub, int m) {
   s.ls = o;     o += (size_t)2 * kTT * m * 4;
   s.li = o;     o += (size_t)2 * kTT * m * 4;
   o = (o + 15) & ~(size_t)15;
-  s.cbuf = o;   o += (size_t)kWaves * kCapMax * 8;
+  s.cbuf = o;   o += (size_t)kWaves * (m * 2 > 64 ? m * 2 : 64) * 8;  // 2k keys per wave
   s.grid = o;   o += (size_t)kGridMax * 4;
   s.rowoff = o; o += (size_t)(m + 1) * 4;
   s.total = o;
@@ -242,7 +241,7 @@ template <int KS>
 __device__ __forceinline__ void mfma_half_scores(const uint16_t* Xb, const uint16_t* Cb,
                                                  int n_sub, int dh, float* sc, int scs,
                                                  int wave, int lane, bool tok_ok) {
-  constexpr int TB = 16 / KS;  // tiles per batch
+  constexpr int TB = 8 / KS;   // tiles per batch
   const int tl = lane & 15;    // token (B column) / sub-key (A row) in the tile
   const int kq = lane >> 4;    // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
@@ -284,7 +283,7 @@ __device__ __forceinline__ void mfma_half_scores(const uint16_t* Xb, const uint1
 }
 
 template <bool BF16, int NPL1, int NPL2>
-__global__ void __launch_bounds__(kThreads, 1) sdm_score_topk_kernel(ScoreArgs a, float zW,
+__global__ void __launch_bounds__(kThreads, 4) sdm_score_topk_kernel(ScoreArgs a, float zW,
                                                                     float zR) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_sub = a.n_sub;
@@ -306,7 +305,7 @@ __global__ void __launch_bounds__(kThreads, 1) sdm_score_topk_kernel(ScoreArgs a
   const int h = st % a.H;
   const int t0 = blockIdx.x * kTT;
   const int dh = a.d_k / 2;
-  uint64_t* buf = cbufs + wave * kCapMax;
+  uint64_t* buf = cbufs + wave * max(64, 2 * mmax);
 
   for (int pass = 0; pass < 2; pass++) {
     const void* X = pass == 0 ? a.kp : a.qp;
@@ -344,7 +343,7 @@ __global__ void __launch_bounds__(kThreads, 1) sdm_score_topk_kernel(ScoreArgs a
       if (BF16) {
         const int tl = lane & 15;
         const int tok = t0 + tl;
-        const bool tok_ok = tok < a.T;
+        const bool tok_ok = tl < kTT && tok < a.T;
         const uint16_t* Xb = static_cast<const uint16_t*>(X) +
                              ((int64_t)st * a.T + (tok_ok ? tok : 0)) * a.d_k + half * dh;
         const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
