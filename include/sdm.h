@@ -83,8 +83,9 @@ typedef struct {
  *   rwt      [B][H][T][R]  fp32    out: read weights
  *
  * Scores are accumulated in fp32 (bf16 products are exact in fp32).
- * Kernel limits (else SDM_ERR_UNSUPPORTED): n_sub <= 1024, d_k/2 a
- * multiple of 16 and <= 256, W, R <= min(n_sub, 128).
+ * Kernel limits (else SDM_ERR_UNSUPPORTED): n_sub a multiple of 16 and
+ * <= 1024, d_k/2 a multiple of 16 and <= 256, W, R <= min(n_sub, 128).
+ * Inputs must be finite.
  */
 int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, const void* kp,
                    const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,

@@ -1,6 +1,4 @@
 // Kernel templates of the product-key addressing (included by the score_topk*.hip units).
-#pragma once
-// Product-key addressing for Sparse Delta Memory, for gfx950.
 //
 // Method ("Sparse Delta Memory", gist.science summaries of paper 2607.07386;
 // Spanish page "Mecanismo Central" item 2, French page "Mecanisme Central"):
@@ -12,22 +10,29 @@
 // descending, ties to the lower index (sub-key index in stage 1, slot in
 // stage 2).
 //
-// One workgroup handles kTT tokens of one (b,h) stream:
-//   1. half scores for the tile: bf16 -> MFMA v_mfma_f32_16x16x32_bf16
-//      (sub-keys x tokens, fp32 accumulate), fp32 -> plain VALU dot products
-//      in the same sequential order as a scalar loop; results to LDS.
-//   2. stage 1, one wave per (token, half): exact top-m selection.
-//   3. stage 2, one wave per token: top-k of the outer sums over the pruned
-//      rank grid {(a,b): (a+1)(b+1) <= k} -- a pair outside it is beaten by at
-//      least k pairs of its dominating rectangle.  With ties in the fp32 sums
-//      that argument can fail, so the best pair just outside the grid is
-//      checked and, if it could compete, the full m x m grid is ranked.
-// Exact selection of the k best of n values held by one wave: every value
-// becomes a unique 64-bit key (order-preserving score bits, then the
-// complemented index), a threshold t with k <= #{key >= t} <= cap is found by
-// counting with ballots (first guess from the score distribution, then integer
-// bisection on keys, which always terminates because keys are unique), the
-// keys >= t are compacted to LDS and sorted by a register bitonic network.
+// One workgroup of 8 waves handles kTT tokens of one (b,h) stream, keys and
+// queries together: column c < kTT is the key of token t0 + c (write list),
+// column kTT + c its query (read list).  Keys and queries are scored against
+// the same sub-key tables, so the 2*kTT = 16 columns fill the N side of a
+// 16x16 MFMA tile and each sub-key is read once per workgroup and half.
+//   1. half scores: sub-keys x columns on v_mfma_f32_16x16x32_bf16 (bf16
+//      inputs, fp32 accumulate) or on the VALU in the sequential order of a
+//      scalar loop (fp32 inputs).  The scores stay in the accumulator
+//      registers: lane (tl, kq) of wave w holds column tl's sub-keys
+//      16*(w + 8*j) + 4*kq + r.
+//   2. stage 1 per column: a threshold t with k <= #{key >= t} <= cap is found
+//      by counting over all waves (first guess from the column's mean and
+//      spread, then bisection on keys), the keys >= t are packed into the
+//      column's LDS candidate buffer and one wave sorts them.
+//   3. stage 2 per column: top-k of the outer sums over the pruned rank grid
+//      {(a,b): (a+1)(b+1) <= k} -- a pair outside it is beaten by at least k
+//      pairs of its dominating rectangle.  With ties in the fp32 sums that
+//      argument can fail, so the best pair just outside the grid is checked
+//      and, if it could compete, the full m x m grid is ranked.
+// Keys are unique 64-bit values (order-preserving score bits, then the
+// complemented index), so every selection is exact and bisection on keys
+// always ends.
+#pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -41,11 +46,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTT = 8;       // tokens per workgroup (MFMA tiles carry 16 columns)
-constexpr int kWaves = 8;    // waves per workgroup
+constexpr int kTT = 8;          // tokens per workgroup
+constexpr int kCols = 2 * kTT;  // key and query columns
+constexpr int kWaves = 8;       // waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kCapMax = 256; // largest candidate set sorted at once
+constexpr int kCapMax = 256;    // largest candidate set sorted at once
 constexpr int kGridMax = 1024;  // largest pruned grid held in registers
+
+// candidates kept for a top-k: between k and this many
+__host__ __device__ inline int cap_for(int k) {
+  const int c = 2 * k > 64 ? 2 * k : 64;
+  return c < kCapMax ? c : kCapMax;
+}
 
 __device__ __forceinline__ uint32_t ord32(float s) {
   uint32_t u = __float_as_uint(s);
@@ -193,340 +205,467 @@ __device__ __forceinline__ int compact_ge(const uint64_t (&key)[NPL], uint64_t t
   return base;
 }
 
-// Exact top-k of the NPL*64 keys of one wave (unused entries hold key 0 and
-// never outrank a real one), delivered in rank order through emit.
-// `guess` is a first threshold estimate (0 = none).
-template <int NPL, typename Emit>
-__device__ void wave_topk(const uint64_t (&key)[NPL], int k, uint64_t guess, uint64_t* buf,
-                          int lane, Emit emit) {
-  uint64_t mx = 0;
-#pragma unroll
-  for (int j = 0; j < NPL; j++) mx = key[j] > mx ? key[j] : mx;
-  mx = wave_max64(mx);
-  const int cap = min(kCapMax, max(64, 2 * k));
-  const uint64_t t = find_threshold(key, k, cap, guess, 0ull, mx + 1ull);
-  const int c = compact_ge(key, t, buf, lane);
-  wave_lds_sync();
-  sort_emit(buf, c, k, lane, emit);
-  wave_lds_sync();
-}
-
 }  // namespace
 
-// Shared-memory layout (bytes), n_sub and m known at launch.
+// Shared-memory layout (bytes) for W write and R read slots.
 struct ScoreSmem {
-  size_t sc, ls, li, cbuf, grid, rowoff, total;
+  size_t ls, li, cand, grid, rowoff, total;
+  int m, capmax, gW, gR;  // list length, candidate stride, grid sizes
 };
 
-__host__ __device__ inline ScoreSmem score_smem(int n_sub, int m) {
+// size of the pruned rank grid {(a,b) : (a+1)(b+1) <= k} over k x k ranks
+__host__ __device__ inline int pruned_grid_size(int k) {
+  int g = 0;
+  for (int a = 0; a < k; a++) g += (k / (a + 1) < k ? k / (a + 1) : k);
+  return g;
+}
+
+__host__ __device__ inline ScoreSmem score_smem(int W, int R) {
   ScoreSmem s;
+  s.m = W > R ? W : R;
+  s.capmax = cap_for(s.m);
+  s.gW = pruned_grid_size(W);
+  s.gR = W == R ? 0 : pruned_grid_size(R);
   size_t o = 0;
-  s.sc = o;     o += (size_t)kTT * (n_sub + 4) * 4;  // rows padded: fewer LDS bank conflicts
-  s.ls = o;     o += (size_t)2 * kTT * m * 4;
-  s.li = o;     o += (size_t)2 * kTT * m * 4;
+  s.ls = o;     o += (size_t)2 * kCols * s.m * 4;  // [half][column][rank] scores
+  s.li = o;     o += (size_t)2 * kCols * s.m * 4;  // [half][column][rank] sub-key ids
   o = (o + 15) & ~(size_t)15;
-  s.cbuf = o;   o += (size_t)kWaves * (m * 2 > 64 ? m * 2 : 64) * 8;  // 2k keys per wave
-  s.grid = o;   o += (size_t)kGridMax * 4;
-  s.rowoff = o; o += (size_t)(m + 1) * 4;
+  s.cand = o;   o += (size_t)kCols * s.capmax * 8;  // [column][capmax] keys
+  s.grid = o;   o += (size_t)(s.gW + s.gR) * 4;     // (ra << 16) | rb, W grid then R grid
+  s.rowoff = o; o += (size_t)2 * (s.m + 1) * 4;
   s.total = o;
   return s;
 }
 
-// Half scores of kTT tokens against all n_sub sub-keys of one half, on MFMA:
-// D[sub-key][token] = sum_k C[sub-key][k] * x[token][k], 16x16 tiles of
-// v_mfma_f32_16x16x32_bf16.  A wave owns sub-key tiles i0 = 16*wave + 128*j;
-// the sub-key fragments of TB tiles are loaded together, so one L2 round trip
-// covers TB tiles.
-template <int KS>
-__device__ __forceinline__ void mfma_half_scores(const uint16_t* Xb, const uint16_t* Cb,
-                                                 int n_sub, int dh, float* sc, int scs,
-                                                 int wave, int lane, bool tok_ok) {
-  constexpr int TB = 8 / KS;   // tiles per batch
-  const int tl = lane & 15;    // token (B column) / sub-key (A row) in the tile
-  const int kq = lane >> 4;    // which 8-wide K chunk of the 32
+namespace {
+
+// Half scores of the 16 columns against this wave's sub-key tiles
+// i0 = 16*(wave + 8*j), j < NT: D[sub-key][column] = sum_e C[sub-key][e] *
+// x[column][e] on v_mfma_f32_16x16x32_bf16.  n_sub is a multiple of 16, so a
+// tile is wholly inside the table or wholly outside (skipped, scores 0).
+// Sub-key rows are read through a buffer resource per tile whose range ends
+// at the table's end: one offset register serves every tile, and the reads
+// past a row's dh elements (dh not a multiple of 32) meet a zero B fragment
+// or, past the table, read as zero.  xcol points at this lane's column half
+// (any valid row when !col_ok).
+template <int NT, int KS>
+__device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, const uint16_t* Cb,
+                                            int n_sub, int dh, int wave, int lane,
+                                            float (&sc)[NT][4]) {
+  constexpr int TB = 8 / KS > 0 ? 8 / KS : 1;  // sub-key tiles loaded together
+  const int tl = lane & 15;  // sub-key row of the A tile, column of the B tile
+  const int kq = lane >> 4;  // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) {
     const int d0 = ks * 32 + kq * 8;
-    bfrag[ks] = (tok_ok && d0 < dh) ? *reinterpret_cast<const bf16x8*>(Xb + d0) : bf16x8{};
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(xcol + min(d0, dh - 8));
+    bfrag[ks] = (col_ok && d0 < dh) ? v : bf16x8{};
   }
-  for (int ib = wave * 16; ib < n_sub; ib += kWaves * 16 * TB) {
+  const int voff = (tl * dh + kq * 8) * 2;  // bytes within a tile
+#pragma unroll
+  for (int j0 = 0; j0 < NT; j0 += TB) {
     bf16x8 af[TB][KS];
 #pragma unroll
     for (int t = 0; t < TB; t++) {
-      const int sk = ib + t * kWaves * 16 + tl;
+      const int i0 = 16 * (wave + kWaves * (j0 + t));
+      if (j0 + t < NT && i0 < n_sub) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Cb + (int64_t)i0 * dh), (short)0, (n_sub - i0) * dh * 2, 0x00020000);
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        const int d0 = ks * 32 + kq * 8;
-        af[t][ks] = (sk < n_sub && d0 < dh)
-                        ? *reinterpret_cast<const bf16x8*>(Cb + (int64_t)sk * dh + d0)
-                        : bf16x8{};
+        for (int ks = 0; ks < KS; ks++) {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + ks * 64, 0, 0);
+          af[t][ks] = __builtin_bit_cast(bf16x8, w);
+        }
       }
     }
 #pragma unroll
     for (int t = 0; t < TB; t++) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int i0 = 16 * (wave + kWaves * (j0 + t));
+      if (j0 + t < NT) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (i0 < n_sub) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][ks], bfrag[ks], acc, 0, 0, 0);
-      // D[row = sub-key i0 + 4*kq + r][col = token tl]
-      const int s0 = ib + t * kWaves * 16 + 4 * kq;
-      if (tok_ok && s0 < n_sub) {
-        if (s0 + 3 < n_sub) {
-          *reinterpret_cast<float4*>(sc + tl * scs + s0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        } else {
-          for (int r = 0; r < 4 && s0 + r < n_sub; r++) sc[tl * scs + s0 + r] = acc[r];
+          for (int ks = 0; ks < KS; ks++)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][ks], bfrag[ks], acc, 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 4; r++) sc[j0 + t][r] = acc[r];
       }
     }
   }
 }
 
-template <bool BF16, int NPL1, int NPL2>
+// fp32 inputs: the same layout, each score a sequential dot product.
+template <int NT>
+__device__ __forceinline__ void valu_scores(const float* xcol, const float* Cf, int n_sub, int dh,
+                                            int wave, int lane, float (&sc)[NT][4]) {
+  const int kq = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NT; j++) {
+    const int i0 = 16 * (wave + kWaves * j);
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      sc[j][r] = i0 < n_sub ? dot_seq(xcol, Cf + (int64_t)(i0 + 4 * kq + r) * dh, dh) : 0.f;
+  }
+}
+
+// #{own keys >= t}; o == 0 marks an empty position.  base_id is the sub-key
+// id of (j = 0, r = 0); position (j, r) holds id base_id + 128*j + r.
+template <int NT>
+__device__ __forceinline__ int count_own(const uint32_t (&o)[NT][4], uint32_t base_id,
+                                         uint64_t t) {
+  int c = 0;
+  const uint32_t th = (uint32_t)(t >> 32);
+  if ((uint32_t)t == 0u) {
+    // keys >= (th, 0) exactly when the score part is >= th
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) c += o[j][r] >= th ? 1 : 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const uint64_t kk = ((uint64_t)o[j][r] << 32) |
+                            (uint64_t)(0xffffffffu - (base_id + kWaves * 16 * j + r));
+        c += (o[j][r] != 0u && kk >= t) ? 1 : 0;
+      }
+  }
+  return c;
+}
+
+// Stage 2 for one column whose stage-1 lists (rank order) are s1/i1, s2/i2:
+// the k best slots over the pruned grid, written in rank order with their
+// softmax weights.  buf holds cap_for(k) keys of scratch.
+template <int NPL2>
+__device__ __forceinline__ void stage2(const float* s1, const int32_t* i1, const float* s2,
+                                       const int32_t* i2, int m, int k, int n_sub,
+                                       const uint32_t* grid, int G, uint64_t* buf, int lane,
+                                       int32_t* dst_i, float* dst_w) {
+  uint64_t key[NPL2];
+#pragma unroll
+  for (int j = 0; j < NPL2; j++) {
+    const int c = j * 64 + lane;
+    key[j] = 0ull;
+    if (c < G) {
+      const uint32_t ab = grid[c];
+      const int ra = ab >> 16, rb = ab & 0xffff;
+      key[j] = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
+    }
+  }
+  const int cap = cap_for(k);
+  uint64_t* sorted = buf;  // sorted keys land back in buf
+  uint64_t kth;            // k-th best key of the pruned grid
+  {
+    uint64_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
+    mx = wave_max64(mx);
+    // first threshold: for any rank ra the rectangle [0..ra] x [0..cb] with
+    // cb = ceil(k/(ra+1)) - 1 holds at least k sums, all at least its
+    // corner's, so the best corner is a lower bound of the k-th sum
+    uint64_t lb = 0ull;
+    for (int ra = lane; ra < m; ra += 64) {
+      const int cb = (k + ra) / (ra + 1) - 1;
+      const uint64_t kk = (uint64_t)ord32(s1[ra] + s2[cb]) << 32;
+      lb = kk > lb ? kk : lb;
+    }
+    lb = wave_max64(lb);
+    const uint64_t t = find_threshold(key, k, cap, lb, 0ull, mx + 1ull);
+    const int c = compact_ge(key, t, buf, lane);
+    wave_lds_sync();
+    sort_emit(buf, c, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
+    wave_lds_sync();
+    kth = sorted[k - 1];
+  }
+  // best pair just outside the pruned grid, row by row
+  uint64_t fr = 0ull;
+  for (int ra = lane; ra < m; ra += 64) {
+    const int rb = min(m, k / (ra + 1));
+    if (rb < m) {
+      const uint64_t kk = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
+      fr = kk > fr ? kk : fr;
+    }
+  }
+  fr = wave_max64(fr);
+  // exact if no outside pair can outrank the k-th: compare scores only,
+  // since a score tie with a lower slot would outrank it
+  const bool exact = fr == 0ull || key_score(fr) < key_score(kth);
+  if (!exact) {
+    // rank the full m x m grid: keys >= kth are the candidates (at least k of
+    // them); bisect upward if there are too many.
+    auto full_key = [&](int q) {
+      const int ra = q / m, rb = q % m;
+      return make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
+    };
+    auto cnt = [&](uint64_t t) {
+      int c = 0;
+      for (int base = 0; base < m * m; base += 64) {
+        const int q = base + lane;
+        c += __popcll(__ballot(q < m * m && full_key(q) >= t));
+      }
+      return c;
+    };
+    uint64_t lo = kth, hi = ~0ull, t = kth;
+    for (int it = 0; it < 96; it++) {
+      const int c = cnt(t);
+      if (c >= k && c <= cap) break;
+      if (c < k) hi = t;
+      else lo = t;
+      if (hi - lo <= 1) {
+        t = lo;
+        break;
+      }
+      t = lo + (hi - lo) / 2;
+    }
+    int base = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int b0 = 0; b0 < m * m; b0 += 64) {
+      const int q = b0 + lane;
+      const uint64_t kk = q < m * m ? full_key(q) : 0ull;
+      const bool f = q < m * m && kk >= t;
+      const uint64_t msk = __ballot(f);
+      if (f) buf[base + __popcll(msk & below)] = kk;
+      base += __popcll(msk);
+    }
+    wave_lds_sync();
+    sort_emit(buf, base, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
+    wave_lds_sync();
+  }
+  // softmax over the k selected sums (rank order, max first)
+  const float top = key_score(sorted[0]);
+  float zsum = 0.f;
+  for (int r = lane; r < k; r += 64) zsum += expf(key_score(sorted[r]) - top);
+  zsum = wave_sum(zsum);
+  for (int r = lane; r < k; r += 64) {
+    const uint64_t kk = sorted[r];
+    dst_i[r] = (int32_t)key_id(kk);
+    dst_w[r] = expf(key_score(kk) - top) / zsum;
+  }
+  wave_lds_sync();
+}
+
+// Row offsets of the pruned grid for k (k <= 128 rows, two per lane) by a
+// prefix sum over one wave; returns the grid size.
+__device__ __forceinline__ int grid_rowoff(int k, int32_t* rowoff, int lane) {
+  const int len0 = lane < k ? min(k, k / (lane + 1)) : 0;
+  const int len1 = lane + 64 < k ? min(k, k / (lane + 65)) : 0;
+  int s0 = len0, s1 = len1;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y0 = __shfl_up(s0, o), y1 = __shfl_up(s1, o);
+    if (lane >= o) s0 += y0, s1 += y1;
+  }
+  const int tot0 = __shfl(s0, 63);
+  if (lane < k) rowoff[lane] = s0 - len0;
+  if (lane + 64 < k) rowoff[lane + 64] = tot0 + s1 - len1;
+  const int G = tot0 + __shfl(s1, 63);
+  if (lane == 0) rowoff[k] = G;
+  return G;
+}
+
+__device__ __forceinline__ void grid_fill(int k, const int32_t* rowoff, uint32_t* grid, int wave,
+                                          int lane) {
+  for (int ra = wave; ra < k; ra += kWaves) {
+    const int off = rowoff[ra], len = rowoff[ra + 1] - off;
+    for (int rb = lane; rb < len; rb += 64) grid[off + rb] = ((uint32_t)ra << 16) | rb;
+  }
+}
+
+template <bool BF16, int NT, int NPL2>
 __global__ void __launch_bounds__(kThreads, 4) sdm_score_topk_kernel(ScoreArgs a, float zW,
                                                                     float zR) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int n_sub = a.n_sub;
-  const int mmax = max(a.W, a.R);
-  const ScoreSmem L = score_smem(n_sub, mmax);
-  float* sc = reinterpret_cast<float*>(smem + L.sc);       // [kTT][n_sub + 4]
-  const int scs = n_sub + 4;
-  float* ls = reinterpret_cast<float*>(smem + L.ls);       // [2][kTT][mmax]
-  int32_t* li = reinterpret_cast<int32_t*>(smem + L.li);   // [2][kTT][mmax]
-  uint64_t* cbufs = reinterpret_cast<uint64_t*>(smem + L.cbuf);
-  uint32_t* grid = reinterpret_cast<uint32_t*>(smem + L.grid);  // (a << 16) | b
+  __shared__ float2 s_stat[kWaves][kCols];    // per wave: sum, sum of squares
+  __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
+  __shared__ int s_cnt[2][kWaves][kCols];     // per wave: #{keys >= t}, two rounds
+  const ScoreSmem L = score_smem(a.W, a.R);
+  const int m = L.m;
+  float* ls = reinterpret_cast<float*>(smem + L.ls);
+  int32_t* li = reinterpret_cast<int32_t*>(smem + L.li);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
+  uint32_t* grid = reinterpret_cast<uint32_t*>(smem + L.grid);
   int32_t* rowoff = reinterpret_cast<int32_t*>(smem + L.rowoff);
-  __shared__ int s_gcount;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int st = blockIdx.y;
   const int h = st % a.H;
   const int t0 = blockIdx.x * kTT;
-  const int dh = a.d_k / 2;
-  uint64_t* buf = cbufs + wave * max(64, 2 * mmax);
 
-  for (int pass = 0; pass < 2; pass++) {
-    const void* X = pass == 0 ? a.kp : a.qp;
-    const int k = pass == 0 ? a.W : a.R;
-    const int m = k;  // stage-1 list length (k <= n_sub)
-    const float z = pass == 0 ? zW : zR;
-    int32_t* oidx = pass == 0 ? a.widx : a.ridx;
-    float* owt = pass == 0 ? a.wwt : a.rwt;
+  // pruned rank grids (R's only when R != W); the row fill is ordered before
+  // stage 2 by the barriers of stage 1
+  if (wave == 0) {
+    grid_rowoff(a.W, rowoff, lane);
+    if (L.gR) grid_rowoff(a.R, rowoff + (m + 1), lane);
+  }
+  __syncthreads();
+  grid_fill(a.W, rowoff, grid, wave, lane);
+  if (L.gR) grid_fill(a.R, rowoff + (m + 1), grid + L.gW, wave, lane);
 
-    // pruned rank grid {(ra, rb) : (ra+1)(rb+1) <= k}, row-major; row
-    // offsets by a prefix sum over wave 0 (m <= 128 rows, two per lane)
-    if (wave == 0) {
-      const int len0 = lane < m ? min(m, k / (lane + 1)) : 0;
-      const int len1 = lane + 64 < m ? min(m, k / (lane + 65)) : 0;
-      int s0 = len0, s1 = len1;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y0 = __shfl_up(s0, o), y1 = __shfl_up(s1, o);
-        if (lane >= o) s0 += y0, s1 += y1;
+  for (int half = 0; half < 2; half++) {
+    // Everything below is derived afresh from these in each half: values
+    // kept live across the halves would not fit in the register budget.
+    int n_sub = a.n_sub, dh = a.d_k / 2, hw = wave, hl = lane;
+    asm volatile("" : "+s"(n_sub), "+s"(dh), "+s"(hw), "+v"(hl));
+    const int tl = hl & 15;  // this lane's column
+    const int kq = hl >> 4;
+    const bool is_q = tl >= kTT;
+    const int tok = t0 + (tl & (kTT - 1));
+    const bool col_ok = tok < a.T;
+    const int kc = is_q ? a.R : a.W;
+    const int capc = cap_for(kc);
+    const float zc = is_q ? zR : zW;
+    const uint32_t base_id = 16u * hw + 4u * kq;  // sub-key id of this lane's first score
+
+    // ---- 1. half scores ---------------------------------------------------
+    float sc[NT][4];
+    if (BF16) {
+      const uint16_t* xcol = static_cast<const uint16_t*>(is_q ? a.qp : a.kp) +
+                             ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
+      const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
+                           ((int64_t)h * 2 + half) * n_sub * dh;
+      if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+      else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+      else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+      else mfma_scores<NT, 8>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+    } else {
+      const float* xcol = static_cast<const float*>(is_q ? a.qp : a.kp) +
+                          ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
+      const float* Cf = static_cast<const float*>(a.subkeys) + ((int64_t)h * 2 + half) * n_sub * dh;
+      valu_scores<NT>(xcol, Cf, n_sub, dh, hw, hl, sc);
+    }
+
+    // ---- 2. stage 1: threshold over all waves, pack, sort -----------------
+    uint32_t o[NT][4];
+    float sum = 0.f, sq = 0.f;
+    uint32_t omax = 0u;
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const bool valid = 16 * (hw + kWaves * j) < n_sub;  // whole tiles
+        const float s = sc[j][r];
+        o[j][r] = valid ? ord32(s) : 0u;
+        sum += valid ? s : 0.f;
+        sq += valid ? s * s : 0.f;
+        omax = o[j][r] > omax ? o[j][r] : omax;
       }
-      const int tot0 = __shfl(s0, 63);
-      const int G = tot0 + __shfl(s1, 63);
-      if (lane < m) rowoff[lane] = s0 - len0;
-      if (lane + 64 < m) rowoff[lane + 64] = tot0 + s1 - len1;
-      if (lane == 0) rowoff[m] = G, s_gcount = G;
+    sum += xor_shuffle(sum, 16, hl);
+    sq += xor_shuffle(sq, 16, hl);
+    omax = max(omax, xor_shuffle(omax, 16, hl));
+    sum += xor_shuffle(sum, 32, hl);
+    sq += xor_shuffle(sq, 32, hl);
+    omax = max(omax, xor_shuffle(omax, 32, hl));
+    if (kq == 0) {
+      s_stat[hw][tl] = make_float2(sum, sq);
+      s_max[hw][tl] = omax;
     }
     __syncthreads();
-    for (int ra = wave; ra < m; ra += kWaves) {
-      const int len = rowoff[ra + 1] - rowoff[ra];
-      for (int rb = lane; rb < len; rb += 64) grid[rowoff[ra] + rb] = ((uint32_t)ra << 16) | rb;
-    }
-
-    for (int half = 0; half < 2; half++) {
-      // ---- 1. half scores of the tile into sc[token][sub-key] -------------
-      __syncthreads();  // previous users of sc are done
-      if (BF16) {
-        const int tl = lane & 15;
-        const int tok = t0 + tl;
-        const bool tok_ok = tl < kTT && tok < a.T;
-        const uint16_t* Xb = static_cast<const uint16_t*>(X) +
-                             ((int64_t)st * a.T + (tok_ok ? tok : 0)) * a.d_k + half * dh;
-        const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
-                             ((int64_t)h * 2 + half) * n_sub * dh;
-        if (dh <= 32) mfma_half_scores<1>(Xb, Cb, n_sub, dh, sc, scs, wave, lane, tok_ok);
-        else if (dh <= 64) mfma_half_scores<2>(Xb, Cb, n_sub, dh, sc, scs, wave, lane, tok_ok);
-        else if (dh <= 128) mfma_half_scores<4>(Xb, Cb, n_sub, dh, sc, scs, wave, lane, tok_ok);
-        else mfma_half_scores<8>(Xb, Cb, n_sub, dh, sc, scs, wave, lane, tok_ok);
-      } else {
-        const float* Xf = static_cast<const float*>(X);
-        const float* Cf = static_cast<const float*>(a.subkeys) +
-                          ((int64_t)h * 2 + half) * n_sub * dh;
-        for (int p = tid; p < kTT * n_sub; p += kThreads) {
-          const int tl = p / n_sub, i = p % n_sub;
-          const int tok = t0 + tl;
-          if (tok >= a.T) continue;
-          const float* x = Xf + ((int64_t)st * a.T + tok) * a.d_k + half * dh;
-          const float* c = Cf + (int64_t)i * dh;
-          sc[tl * scs + i] = dot_seq(x, c, dh);
-        }
-      }
-      __syncthreads();
-
-      // ---- 2. stage 1: top-m sub-keys of each token's half ----------------
-      for (int tl = wave; tl < kTT; tl += kWaves) {
-        if (t0 + tl >= a.T) continue;
-        const float* row = sc + tl * scs;
-        uint64_t key[NPL1];
-        float sum = 0.f, sq = 0.f;
+    sum = 0.f, sq = 0.f, omax = 0u;
 #pragma unroll
-        for (int j = 0; j < NPL1; j++) {
-          const int i = j * 64 + lane;
-          if (i < n_sub) {
-            const float s = row[i];
-            key[j] = make_key(s, (uint32_t)i);
-            sum += s;
-            sq += s * s;
-          } else {
-            key[j] = 0ull;
-          }
+    for (int w = 0; w < kWaves; w++) {
+      const float2 v = s_stat[w][tl];
+      sum += v.x;
+      sq += v.y;
+      omax = max(omax, s_max[w][tl]);
+    }
+    const float mean = sum / n_sub;
+    const float sd = sqrtf(fmaxf(sq / n_sub - mean * mean, 0.f));
+    uint64_t lo = 0ull, hi = ((uint64_t)omax + 1ull) << 32;
+    const uint64_t guess = (uint64_t)ord32(mean + zc * sd) << 32;
+    uint64_t t = (guess > lo && guess < hi) ? guess : lo + (hi - lo) / 2;
+    int it = 0, own = 0;
+    for (;;) {
+      // keys are rebuilt from o in every round, not kept live across rounds
+#pragma unroll
+      for (int j = 0; j < NT; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) asm volatile("" : "+v"(o[j][r]));
+      own = count_own<NT>(o, base_id, t);
+      int ws = own + (int)xor_shuffle((uint32_t)own, 16, hl);
+      ws += (int)xor_shuffle((uint32_t)ws, 32, hl);
+      if (kq == 0) s_cnt[it & 1][hw][tl] = ws;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; w++) tot += s_cnt[it & 1][w][tl];
+      const bool ok = !col_ok || (tot >= kc && tot <= capc);
+      if (__ballot(!ok) == 0ull || it >= 127) break;  // same decision in every wave
+      if (!ok) {
+        if (tot < kc) hi = t;
+        else lo = t;
+        t = hi - lo <= 1 ? lo : lo + (hi - lo) / 2;
+      }
+      it++;
+    }
+    const int fin = it & 1;
+    // pack this lane's keys >= t behind those of earlier waves and lanes
+    int pos = 0;
+    for (int w = 0; w < hw; w++) pos += s_cnt[fin][w][tl];
+    {
+      const int x16 = (int)xor_shuffle((uint32_t)own, 16, hl);  // kq ^ 1
+      const int x32 = (int)xor_shuffle((uint32_t)own, 32, hl);  // kq ^ 2
+      const int x48 = (int)xor_shuffle((uint32_t)x16, 32, hl);  // kq ^ 3
+      pos += kq == 0 ? 0 : kq == 1 ? x16 : kq == 2 ? x32 + x48 : x16 + x32 + x48;
+    }
+    if (col_ok) {
+      uint64_t* cb = cand + tl * L.capmax;
+#pragma unroll
+      for (int j = 0; j < NT; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const uint64_t kk = ((uint64_t)o[j][r] << 32) |
+                              (uint64_t)(0xffffffffu - (base_id + kWaves * 16 * j + r));
+          if (o[j][r] != 0u && kk >= t && pos < L.capmax) cb[pos++] = kk;
         }
-        sum = wave_sum(sum);
-        sq = wave_sum(sq);
-        const float mean = sum / n_sub;
-        const float sd = sqrtf(fmaxf(sq / n_sub - mean * mean, 0.f));
-        const uint64_t guess = (uint64_t)ord32(mean + z * sd) << 32;
-        float* ols = ls + (half * kTT + tl) * mmax;
-        int32_t* oli = li + (half * kTT + tl) * mmax;
-        wave_topk(key, m, guess, buf, lane, [&](int r, uint64_t kk) {
+    }
+    __syncthreads();
+    // one wave per column sorts: wave w owns the key and query columns of token t0 + w
+    if (t0 + hw < a.T) {
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int cc = hw + q * kTT;
+        const int k = q ? a.R : a.W;
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
+        c = min(c, L.capmax);
+        float* ols = ls + (half * kCols + cc) * m;
+        int32_t* oli = li + (half * kCols + cc) * m;
+        sort_emit(cand + cc * L.capmax, c, k, hl, [&](int r, uint64_t kk) {
           ols[r] = key_score(kk);
           oli[r] = (int32_t)key_id(kk);
         });
+        wave_lds_sync();
       }
     }
-    __syncthreads();  // both halves' lists complete
+  }
 
-    // ---- 3. stage 2: top-k slots of the outer sums -------------------------
-    const int G = s_gcount;
-    for (int tl = wave; tl < kTT; tl += kWaves) {
-      const int tok = t0 + tl;
-      if (tok >= a.T) continue;
-      const float* s1 = ls + (0 * kTT + tl) * mmax;
-      const float* s2 = ls + (1 * kTT + tl) * mmax;
-      const int32_t* i1 = li + (0 * kTT + tl) * mmax;
-      const int32_t* i2 = li + (1 * kTT + tl) * mmax;
-      uint64_t key[NPL2];
+  // ---- 3. stage 2: this wave's two columns (lists written by this wave) ----
+  __syncthreads();  // grid rows filled by every wave
+  const int n_sub = a.n_sub;
+  const int tw = t0 + wave;
+  if (tw < a.T) {
 #pragma unroll
-      for (int j = 0; j < NPL2; j++) {
-        const int c = j * 64 + lane;
-        key[j] = 0ull;
-        if (c < G) {
-          const uint32_t ab = grid[c];
-          const int ra = ab >> 16, rb = ab & 0xffff;
-          key[j] = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
-        }
-      }
-      // linear first guess between the extremes of the candidate scores
-      uint64_t kth = 0ull;  // k-th best key of the pruned grid
-      int32_t* dst_i = oidx + ((int64_t)st * a.T + tok) * k;
-      float* dst_w = owt + ((int64_t)st * a.T + tok) * k;
-      uint64_t* sorted = buf;  // reused below: sorted keys land here first
-      {
-        uint64_t mx = 0;
-#pragma unroll
-        for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
-        mx = wave_max64(mx);
-        const int cap = min(kCapMax, max(64, 2 * k));
-        // first threshold: for any rank ra the rectangle [0..ra] x [0..cb] with
-        // cb = ceil(k/(ra+1)) - 1 holds at least k sums, all at least its
-        // corner's, so the best corner is a lower bound of the k-th sum
-        uint64_t lb = 0ull;
-        for (int ra = lane; ra < m; ra += 64) {
-          const int cb = (k + ra) / (ra + 1) - 1;
-          const uint64_t kk = (uint64_t)ord32(s1[ra] + s2[cb]) << 32;
-          lb = kk > lb ? kk : lb;
-        }
-        lb = wave_max64(lb);
-        const uint64_t t = find_threshold(key, k, cap, lb, 0ull, mx + 1ull);
-        const int c = compact_ge(key, t, buf, lane);
-        wave_lds_sync();
-        // sort in place: emit writes back into buf positions < k
-        sort_emit(buf, c, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
-        wave_lds_sync();
-        kth = sorted[k - 1];
-      }
-      // best pair just outside the pruned grid, row by row
-      uint64_t fr = 0ull;
-      for (int ra = lane; ra < m; ra += 64) {
-        const int rb = min(m, k / (ra + 1));
-        if (rb < m) {
-          const uint64_t kk = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
-          fr = kk > fr ? kk : fr;
-        }
-      }
-      fr = wave_max64(fr);
-      // exact if no outside pair can outrank the k-th: compare scores only,
-      // since a score tie with a lower slot would outrank it
-      const bool exact = fr == 0ull || key_score(fr) < key_score(kth);
-      if (!exact) {
-        // rank the full m x m grid: keys >= kth are the candidates (at least
-        // k of them); bisect upward if there are too many.
-        const int cap = min(kCapMax, max(64, 2 * k));
-        auto cnt = [&](uint64_t t) {
-          int c = 0;
-          for (int base = 0; base < m * m; base += 64) {
-            const int q = base + lane;
-            bool f = false;
-            if (q < m * m) {
-              const int ra = q / m, rb = q % m;
-              f = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb])) >= t;
-            }
-            c += __popcll(__ballot(f));
-          }
-          return c;
-        };
-        uint64_t lo = kth, hi = ~0ull, t = kth;
-        for (int it = 0; it < 96; it++) {
-          const int c = cnt(t);
-          if (c >= k && c <= cap) break;
-          if (c < k) hi = t;
-          else lo = t;
-          if (hi - lo <= 1) {
-            t = lo;
-            break;
-          }
-          t = lo + (hi - lo) / 2;
-        }
-        int base = 0;
-        const uint64_t below = (1ull << lane) - 1ull;
-        for (int b0 = 0; b0 < m * m; b0 += 64) {
-          const int q = b0 + lane;
-          uint64_t kk = 0ull;
-          if (q < m * m) {
-            const int ra = q / m, rb = q % m;
-            kk = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
-          }
-          const bool f = q < m * m && kk >= t;
-          const uint64_t msk = __ballot(f);
-          if (f) buf[base + __popcll(msk & below)] = kk;
-          base += __popcll(msk);
-        }
-        wave_lds_sync();
-        sort_emit(buf, base, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
-        wave_lds_sync();
-      }
-      // softmax over the k selected sums (rank order, max first)
-      const float top = key_score(sorted[0]);
-      float zsum = 0.f;
-      for (int r = lane; r < k; r += 64) zsum += expf(key_score(sorted[r]) - top);
-      zsum = wave_sum(zsum);
-      for (int r = lane; r < k; r += 64) {
-        const uint64_t kk = sorted[r];
-        dst_i[r] = (int32_t)key_id(kk);
-        dst_w[r] = expf(key_score(kk) - top) / zsum;
-      }
-      wave_lds_sync();
+    for (int q = 0; q < 2; q++) {
+      const int cc = wave + q * kTT;
+      const int k = q ? a.R : a.W;
+      const bool own_grid = q && L.gR;
+      stage2<NPL2>(ls + cc * m, li + cc * m, ls + (kCols + cc) * m, li + (kCols + cc) * m, k, k,
+                   n_sub, own_grid ? grid + L.gW : grid, own_grid ? L.gR : L.gW,
+                   cand + cc * L.capmax, lane,
+                   (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,
+                   (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
     }
-    __syncthreads();  // lists and grid are rebuilt by the next pass
   }
 }
 
-// Inverse of the standard normal CDF (rational approximation, relative error
-// about 1e-9; only steers the first threshold guess).
+// Inverse of the standard normal CDF (P. J. Acklam's published rational
+// approximation, relative error about 1e-9); it only steers the first
+// threshold guess.
 static inline double norm_quantile(double p) {
   static const double a[] = {-3.969683028665376e+01, 2.209460984245205e+02,
                              -2.759285104469687e+02, 1.383577518672690e+02,
@@ -564,17 +703,10 @@ static inline float guess_z(int k, int n) {
   return (float)norm_quantile(1.0 - f);
 }
 
-// size of the pruned rank grid {(a,b) : (a+1)(b+1) <= k} over k x k ranks
-static inline int pruned_grid_size(int k) {
-  int g = 0;
-  for (int a = 0; a < k; a++) g += (k / (a + 1) < k ? k / (a + 1) : k);
-  return g;
-}
-
-template <bool BF16, int NPL1, int NPL2>
+template <bool BF16, int NT, int NPL2>
 static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
-  const ScoreSmem L = score_smem(a.n_sub, a.W > a.R ? a.W : a.R);
-  auto k = sdm_score_topk_kernel<BF16, NPL1, NPL2>;
+  const ScoreSmem L = score_smem(a.W, a.R);
+  auto k = sdm_score_topk_kernel<BF16, NT, NPL2>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
@@ -584,11 +716,13 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Launch for one stage-1 width NPL1 (scores per lane), any stage-2 width.
-template <int NPL1>
-hipError_t launch_score_n(const ScoreArgs& a, bool bf16, int npl2, hipStream_t stream) {
+}  // namespace
+
+// Launch for NT sub-key tiles per wave (n_sub <= 128*NT), any grid width.
+template <int NT>
+hipError_t launch_score_t(const ScoreArgs& a, bool bf16, int npl2, hipStream_t stream) {
 #define SDM_SCORE_CASE(M_)                                                      \
-  if (npl2 <= M_) return bf16 ? launch_t<true, NPL1, M_>(a, stream) : launch_t<false, NPL1, M_>(a, stream);
+  if (npl2 <= M_) return bf16 ? launch_t<true, NT, M_>(a, stream) : launch_t<false, NT, M_>(a, stream);
   SDM_SCORE_CASE(4)
   SDM_SCORE_CASE(8)
   SDM_SCORE_CASE(12)

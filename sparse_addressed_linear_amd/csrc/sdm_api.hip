@@ -44,7 +44,7 @@ int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const 
   if (d->T > 0 && (!qp || !kp || !widx || !wwt || !ridx || !rwt)) return SDM_ERR_NULL;
   if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
   const int dh = d->d_k / 2;
-  if (d->n_sub > 1024 || dh % 16 != 0 || dh > 256 || d->W > d->n_sub || d->R > d->n_sub ||
+  if (d->n_sub > 1024 || d->n_sub % 16 != 0 || dh % 16 != 0 || dh > 256 || d->W > d->n_sub || d->R > d->n_sub ||
       d->W > 128 || d->R > 128)
     return SDM_ERR_UNSUPPORTED;
   if (sdm::score_topk_lds_bytes(d->n_sub, d->W, d->R) > kMaxLds) return SDM_ERR_UNSUPPORTED;

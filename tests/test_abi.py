@@ -69,6 +69,7 @@ def test_score_topk_rejects(L):
     assert score(L, dims(n_sub=50000)) == 2     # N >= 2^31
     assert score(L, dims(), dt=7) == 3
     assert score(L, dims(n_sub=2048, W=8)) == 4  # kernel limits
+    assert score(L, dims(n_sub=40, W=8)) == 4    # n_sub not a multiple of 16
     assert score(L, dims(d_k=40)) == 4          # half not a multiple of 16
     assert score(L, dims(W=33)) == 4            # W > n_sub
     assert score(L, dims(n_sub=256, W=129, R=8)) == 4
