@@ -51,7 +51,7 @@ constexpr int kCols = 2 * kTT;  // key and query columns
 constexpr int kWaves = 8;       // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kCapMax = 256;    // largest candidate set sorted at once
-constexpr int kGridMax = 1024;  // largest pruned grid held in registers
+constexpr int kGridMax = 704;   // largest pruned grid held in registers (11 per lane)
 
 // candidates kept for a top-k: between k and this many
 __host__ __device__ inline int cap_for(int k) {
@@ -207,9 +207,12 @@ __device__ __forceinline__ int compact_ge(const uint64_t (&key)[NPL], uint64_t t
 
 }  // namespace
 
-// Shared-memory layout (bytes) for W write and R read slots.
+// Shared-memory layout (bytes) for W write and R read slots.  Column c owns
+// a block of 2*capmax keys: stage-1 candidates of half h at [h*capmax, ...),
+// then, once sorted, the two rank-ordered lists at [0, m) and [m, 2m) and
+// stage 2's scratch at [2m, 2m + capmax) (capmax >= 2m).
 struct ScoreSmem {
-  size_t ls, li, cand, grid, rowoff, total;
+  size_t cand, grid, rowoff, total;
   int m, capmax, gW, gR;  // list length, candidate stride, grid sizes
 };
 
@@ -227,11 +230,8 @@ __host__ __device__ inline ScoreSmem score_smem(int W, int R) {
   s.gW = pruned_grid_size(W);
   s.gR = W == R ? 0 : pruned_grid_size(R);
   size_t o = 0;
-  s.ls = o;     o += (size_t)2 * kCols * s.m * 4;  // [half][column][rank] scores
-  s.li = o;     o += (size_t)2 * kCols * s.m * 4;  // [half][column][rank] sub-key ids
-  o = (o + 15) & ~(size_t)15;
-  s.cand = o;   o += (size_t)kCols * s.capmax * 8;  // [column][capmax] keys
-  s.grid = o;   o += (size_t)(s.gW + s.gR) * 4;     // (ra << 16) | rb, W grid then R grid
+  s.cand = o;   o += (size_t)kCols * 2 * s.capmax * 8;
+  s.grid = o;   o += (size_t)(s.gW + s.gR) * 4;  // (ra << 16) | rb, W grid then R grid
   s.rowoff = o; o += (size_t)2 * (s.m + 1) * 4;
   s.total = o;
   return s;
@@ -325,26 +325,93 @@ __device__ __forceinline__ int count_own(const uint32_t (&o)[NT][4], uint32_t ba
 #pragma unroll
       for (int r = 0; r < 4; r++) c += o[j][r] >= th ? 1 : 0;
   } else {
+    // (o, ~id) >= (th, tlo) with 32-bit compares; o == 0 never reaches th
+    const uint32_t tlo = (uint32_t)t;
 #pragma unroll
     for (int j = 0; j < NT; j++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const uint64_t kk = ((uint64_t)o[j][r] << 32) |
-                            (uint64_t)(0xffffffffu - (base_id + kWaves * 16 * j + r));
-        c += (o[j][r] != 0u && kk >= t) ? 1 : 0;
+        const uint32_t lid = 0xffffffffu - (base_id + kWaves * 16 * j + r);
+        c += (o[j][r] > th || (o[j][r] == th && lid >= tlo)) ? 1 : 0;
       }
   }
   return c;
 }
 
-// Stage 2 for one column whose stage-1 lists (rank order) are s1/i1, s2/i2:
+// Sorted positions p = lane*E + r < k of stage 2: slot ids and softmax
+// weights straight from the registers of the sort.
+template <int E>
+__device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int lane,
+                                           int32_t* dst_i, float* dst_w) {
+  const uint32_t top_hi = __builtin_amdgcn_readfirstlane((uint32_t)(v[0] >> 32));
+  const float top = unord32(top_hi);
+  float e[E];
+  float z = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int p = lane * E + r;
+    e[r] = p < k ? expf(key_score(v[r]) - top) : 0.f;
+    z += e[r];
+  }
+  z = wave_sum(z);
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int p = lane * E + r;
+    if (p < k) {
+      dst_i[p] = (int32_t)key_id(v[r]);
+      dst_w[p] = e[r] / z;
+    }
+  }
+}
+
+// Stage 2 tail once the c candidates in buf are known: sort them in
+// registers, check the frontier outside the pruned grid, write the result.
+// Returns false when the frontier could compete (the caller then ranks the
+// full grid).
+template <int E>
+__device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, const uint64_t* L1,
+                                              const uint64_t* L2, int m, int k, int n_sub,
+                                              int lane, int32_t* dst_i, float* dst_w) {
+  uint64_t v[E];
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int i = lane * E + r;
+    v[r] = i < c ? buf[i] : 0ull;
+  }
+  bitonic_desc<E>(v, lane);
+  // k-th best key: position k-1 = lane (k-1)/E, register (k-1)%E
+  uint64_t kv = v[0];
+#pragma unroll
+  for (int r = 1; r < E; r++) kv = ((k - 1) % E == r) ? v[r] : kv;
+  const int src = (k - 1) / E;
+  const uint32_t klo = __shfl((uint32_t)kv, src), khi = __shfl((uint32_t)(kv >> 32), src);
+  const float kth_score = unord32(khi);
+  (void)klo;
+  // best pair just outside the pruned grid, row by row: exact if it cannot
+  // outrank the k-th (compare scores: a score tie with a lower slot would)
+  float fr = -INFINITY;
+  bool any = false;
+  for (int ra = lane; ra < m; ra += 64) {
+    const int rb = min(m, k / (ra + 1));
+    if (rb < m) {
+      const float s = key_score(L1[ra]) + key_score(L2[rb]);
+      fr = any ? fmaxf(fr, s) : s;
+      any = true;
+    }
+  }
+  const bool compete = __ballot(any && !(fr < kth_score)) != 0ull;
+  if (compete) return false;
+  emit_slots<E>(v, k, lane, dst_i, dst_w);
+  return true;
+}
+
+// Stage 2 for one column whose stage-1 lists (rank-ordered keys) are L1, L2:
 // the k best slots over the pruned grid, written in rank order with their
 // softmax weights.  buf holds cap_for(k) keys of scratch.
 template <int NPL2>
-__device__ __forceinline__ void stage2(const float* s1, const int32_t* i1, const float* s2,
-                                       const int32_t* i2, int m, int k, int n_sub,
-                                       const uint32_t* grid, int G, uint64_t* buf, int lane,
-                                       int32_t* dst_i, float* dst_w) {
+__device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, int m, int k,
+                                       int n_sub, const uint32_t* grid, int G, uint64_t* buf,
+                                       int lane, int32_t* dst_i, float* dst_w) {
   uint64_t key[NPL2];
 #pragma unroll
   for (int j = 0; j < NPL2; j++) {
@@ -352,105 +419,88 @@ __device__ __forceinline__ void stage2(const float* s1, const int32_t* i1, const
     key[j] = 0ull;
     if (c < G) {
       const uint32_t ab = grid[c];
-      const int ra = ab >> 16, rb = ab & 0xffff;
-      key[j] = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
+      const uint64_t a1 = L1[ab >> 16], a2 = L2[ab & 0xffff];
+      key[j] = make_key(key_score(a1) + key_score(a2), key_id(a1) * (uint32_t)n_sub + key_id(a2));
     }
   }
   const int cap = cap_for(k);
-  uint64_t* sorted = buf;  // sorted keys land back in buf
-  uint64_t kth;            // k-th best key of the pruned grid
-  {
-    uint64_t mx = 0;
+  uint64_t mx = 0;
 #pragma unroll
-    for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
-    mx = wave_max64(mx);
-    // first threshold: for any rank ra the rectangle [0..ra] x [0..cb] with
-    // cb = ceil(k/(ra+1)) - 1 holds at least k sums, all at least its
-    // corner's, so the best corner is a lower bound of the k-th sum
-    uint64_t lb = 0ull;
-    for (int ra = lane; ra < m; ra += 64) {
-      const int cb = (k + ra) / (ra + 1) - 1;
-      const uint64_t kk = (uint64_t)ord32(s1[ra] + s2[cb]) << 32;
-      lb = kk > lb ? kk : lb;
-    }
-    lb = wave_max64(lb);
-    const uint64_t t = find_threshold(key, k, cap, lb, 0ull, mx + 1ull);
-    const int c = compact_ge(key, t, buf, lane);
-    wave_lds_sync();
-    sort_emit(buf, c, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
-    wave_lds_sync();
-    kth = sorted[k - 1];
-  }
-  // best pair just outside the pruned grid, row by row
-  uint64_t fr = 0ull;
+  for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
+  mx = wave_max64(mx);
+  // first threshold: for any rank ra the rectangle [0..ra] x [0..cb] with
+  // cb = ceil(k/(ra+1)) - 1 holds at least k sums, all at least its corner's,
+  // so the best corner is a lower bound of the k-th sum
+  uint64_t lb = 0ull;
   for (int ra = lane; ra < m; ra += 64) {
-    const int rb = min(m, k / (ra + 1));
-    if (rb < m) {
-      const uint64_t kk = make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
-      fr = kk > fr ? kk : fr;
-    }
+    const int cb = (k + ra) / (ra + 1) - 1;
+    const uint64_t kk = (uint64_t)ord32(key_score(L1[ra]) + key_score(L2[cb])) << 32;
+    lb = kk > lb ? kk : lb;
   }
-  fr = wave_max64(fr);
-  // exact if no outside pair can outrank the k-th: compare scores only,
-  // since a score tie with a lower slot would outrank it
-  const bool exact = fr == 0ull || key_score(fr) < key_score(kth);
-  if (!exact) {
-    // rank the full m x m grid: keys >= kth are the candidates (at least k of
-    // them); bisect upward if there are too many.
-    auto full_key = [&](int q) {
-      const int ra = q / m, rb = q % m;
-      return make_key(s1[ra] + s2[rb], (uint32_t)(i1[ra] * n_sub + i2[rb]));
-    };
-    auto cnt = [&](uint64_t t) {
-      int c = 0;
-      for (int base = 0; base < m * m; base += 64) {
-        const int q = base + lane;
-        c += __popcll(__ballot(q < m * m && full_key(q) >= t));
-      }
-      return c;
-    };
-    uint64_t lo = kth, hi = ~0ull, t = kth;
-    for (int it = 0; it < 96; it++) {
-      const int c = cnt(t);
-      if (c >= k && c <= cap) break;
-      if (c < k) hi = t;
-      else lo = t;
-      if (hi - lo <= 1) {
-        t = lo;
-        break;
-      }
-      t = lo + (hi - lo) / 2;
+  lb = wave_max64(lb);
+  const uint64_t t = find_threshold(key, k, cap, lb, 0ull, mx + 1ull);
+  const int c = compact_ge(key, t, buf, lane);
+  wave_lds_sync();
+  bool done;
+  if (c <= 64) done = stage2_sorted<1>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  else if (c <= 128) done = stage2_sorted<2>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  else done = stage2_sorted<4>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  if (done) return;
+
+  // rare: rank the full m x m grid.  The k-th key of the pruned grid is a
+  // lower bound; bisect upward until at most cap keys remain.
+  wave_lds_sync();
+  auto full_key = [&](int q) {
+    const uint64_t a1 = L1[q / m], a2 = L2[q % m];
+    return make_key(key_score(a1) + key_score(a2), key_id(a1) * (uint32_t)n_sub + key_id(a2));
+  };
+  auto cnt = [&](uint64_t tt) {
+    int n = 0;
+    for (int base = 0; base < m * m; base += 64) {
+      const int q = base + lane;
+      n += __popcll(__ballot(q < m * m && full_key(q) >= tt));
     }
-    int base = 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int b0 = 0; b0 < m * m; b0 += 64) {
-      const int q = b0 + lane;
-      const uint64_t kk = q < m * m ? full_key(q) : 0ull;
-      const bool f = q < m * m && kk >= t;
-      const uint64_t msk = __ballot(f);
-      if (f) buf[base + __popcll(msk & below)] = kk;
-      base += __popcll(msk);
+    return n;
+  };
+  uint64_t lo = 0ull, hi = ~0ull, tt = t;
+  for (int it = 0; it < 96; it++) {
+    const int n = cnt(tt);
+    if (n >= k && n <= cap) break;
+    if (n < k) hi = tt;
+    else lo = tt;
+    if (hi - lo <= 1) {
+      tt = lo;
+      break;
     }
-    wave_lds_sync();
-    sort_emit(buf, base, k, lane, [&](int r, uint64_t kk) { sorted[r] = kk; });
-    wave_lds_sync();
+    tt = lo + (hi - lo) / 2;
   }
-  // softmax over the k selected sums (rank order, max first)
-  const float top = key_score(sorted[0]);
-  float zsum = 0.f;
-  for (int r = lane; r < k; r += 64) zsum += expf(key_score(sorted[r]) - top);
-  zsum = wave_sum(zsum);
-  for (int r = lane; r < k; r += 64) {
-    const uint64_t kk = sorted[r];
-    dst_i[r] = (int32_t)key_id(kk);
-    dst_w[r] = expf(key_score(kk) - top) / zsum;
+  int base = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int b0 = 0; b0 < m * m; b0 += 64) {
+    const int q = b0 + lane;
+    const uint64_t kk = q < m * m ? full_key(q) : 0ull;
+    const bool f = q < m * m && kk >= tt;
+    const uint64_t msk = __ballot(f);
+    if (f) buf[base + __popcll(msk & below)] = kk;
+    base += __popcll(msk);
   }
   wave_lds_sync();
+  sort_emit(buf, base, k, lane, [&](int r, uint64_t kk) { buf[r] = kk; });
+  wave_lds_sync();
+  const float top = key_score(buf[0]);
+  float z = 0.f;
+  for (int r = lane; r < k; r += 64) z += expf(key_score(buf[r]) - top);
+  z = wave_sum(z);
+  for (int r = lane; r < k; r += 64) {
+    const uint64_t kk = buf[r];
+    dst_i[r] = (int32_t)key_id(kk);
+    dst_w[r] = expf(key_score(kk) - top) / z;
+  }
 }
 
 // Row offsets of the pruned grid for k (k <= 128 rows, two per lane) by a
-// prefix sum over one wave; returns the grid size.
-__device__ __forceinline__ int grid_rowoff(int k, int32_t* rowoff, int lane) {
+// prefix sum over one wave.
+__device__ __forceinline__ void grid_rowoff(int k, int32_t* rowoff, int lane) {
   const int len0 = lane < k ? min(k, k / (lane + 1)) : 0;
   const int len1 = lane + 64 < k ? min(k, k / (lane + 65)) : 0;
   int s0 = len0, s1 = len1;
@@ -461,9 +511,7 @@ __device__ __forceinline__ int grid_rowoff(int k, int32_t* rowoff, int lane) {
   const int tot0 = __shfl(s0, 63);
   if (lane < k) rowoff[lane] = s0 - len0;
   if (lane + 64 < k) rowoff[lane + 64] = tot0 + s1 - len1;
-  const int G = tot0 + __shfl(s1, 63);
-  if (lane == 0) rowoff[k] = G;
-  return G;
+  if (lane == 0) rowoff[k] = tot0 + __shfl(s1, 63);
 }
 
 __device__ __forceinline__ void grid_fill(int k, const int32_t* rowoff, uint32_t* grid, int wave,
@@ -475,16 +523,14 @@ __device__ __forceinline__ void grid_fill(int k, const int32_t* rowoff, uint32_t
 }
 
 template <bool BF16, int NT, int NPL2>
-__global__ void __launch_bounds__(kThreads, 4) sdm_score_topk_kernel(ScoreArgs a, float zW,
-                                                                    float zR) {
+__global__ void __launch_bounds__(kThreads, 4)
+    sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, float zW, float zR) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float2 s_stat[kWaves][kCols];    // per wave: sum, sum of squares
   __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
   __shared__ int s_cnt[2][kWaves][kCols];     // per wave: #{keys >= t}, two rounds
   const ScoreSmem L = score_smem(a.W, a.R);
-  const int m = L.m;
-  float* ls = reinterpret_cast<float*>(smem + L.ls);
-  int32_t* li = reinterpret_cast<int32_t*>(smem + L.li);
+  const int m = L.m, cm = L.capmax;
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
   uint32_t* grid = reinterpret_cast<uint32_t*>(smem + L.grid);
   int32_t* rowoff = reinterpret_cast<int32_t*>(smem + L.rowoff);
@@ -493,10 +539,9 @@ __global__ void __launch_bounds__(kThreads, 4) sdm_score_topk_kernel(ScoreArgs a
   const int lane = threadIdx.x & 63;
   const int st = blockIdx.y;
   const int h = st % a.H;
-  const int t0 = blockIdx.x * kTT;
 
-  // pruned rank grids (R's only when R != W); the row fill is ordered before
-  // stage 2 by the barriers of stage 1
+  // pruned rank grids (R's only when R != W), built once per workgroup; the
+  // row fill is ordered before stage 2 by the barriers of stage 1
   if (wave == 0) {
     grid_rowoff(a.W, rowoff, lane);
     if (L.gR) grid_rowoff(a.R, rowoff + (m + 1), lane);
@@ -505,160 +550,164 @@ __global__ void __launch_bounds__(kThreads, 4) sdm_score_topk_kernel(ScoreArgs a
   grid_fill(a.W, rowoff, grid, wave, lane);
   if (L.gR) grid_fill(a.R, rowoff + (m + 1), grid + L.gW, wave, lane);
 
-  for (int half = 0; half < 2; half++) {
-    // Everything below is derived afresh from these in each half: values
-    // kept live across the halves would not fit in the register budget.
-    int n_sub = a.n_sub, dh = a.d_k / 2, hw = wave, hl = lane;
-    asm volatile("" : "+s"(n_sub), "+s"(dh), "+s"(hw), "+v"(hl));
-    const int tl = hl & 15;  // this lane's column
-    const int kq = hl >> 4;
-    const bool is_q = tl >= kTT;
-    const int tok = t0 + (tl & (kTT - 1));
-    const bool col_ok = tok < a.T;
-    const int kc = is_q ? a.R : a.W;
-    const int capc = cap_for(kc);
-    const float zc = is_q ? zR : zW;
-    const uint32_t base_id = 16u * hw + 4u * kq;  // sub-key id of this lane's first score
+  const int ntiles = (a.T + kTT - 1) / kTT;
+  const int tile_end = min(ntiles, (int)(blockIdx.x + 1) * tiles_per_wg);
+  for (int tile = blockIdx.x * tiles_per_wg; tile < tile_end; tile++) {
+    const int t0 = tile * kTT;
+    for (int half = 0; half < 2; half++) {
+      // Everything below is derived afresh from these in each half: values
+      // kept live across halves would not fit in the register budget.
+      int n_sub = a.n_sub, dh = a.d_k / 2, hw = wave, hl = lane;
+      asm volatile("" : "+s"(n_sub), "+s"(dh), "+s"(hw), "+v"(hl));
+      const int tl = hl & 15;  // this lane's column
+      const int kq = hl >> 4;
+      const bool is_q = tl >= kTT;
+      const int tok = t0 + (tl & (kTT - 1));
+      const bool col_ok = tok < a.T;
+      const int kc = is_q ? a.R : a.W;
+      const int capc = cap_for(kc);
+      const float zc = is_q ? zR : zW;
+      const uint32_t base_id = 16u * hw + 4u * kq;  // sub-key id of this lane's first score
 
-    // ---- 1. half scores ---------------------------------------------------
-    float sc[NT][4];
-    if (BF16) {
-      const uint16_t* xcol = static_cast<const uint16_t*>(is_q ? a.qp : a.kp) +
-                             ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
-      const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
-                           ((int64_t)h * 2 + half) * n_sub * dh;
-      if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-      else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-      else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-      else mfma_scores<NT, 8>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-    } else {
-      const float* xcol = static_cast<const float*>(is_q ? a.qp : a.kp) +
-                          ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
-      const float* Cf = static_cast<const float*>(a.subkeys) + ((int64_t)h * 2 + half) * n_sub * dh;
-      valu_scores<NT>(xcol, Cf, n_sub, dh, hw, hl, sc);
-    }
+      // ---- 1. half scores ---------------------------------------------------
+      float sc[NT][4];
+      if (BF16) {
+        const uint16_t* xcol = static_cast<const uint16_t*>(is_q ? a.qp : a.kp) +
+                               ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
+        const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
+                             ((int64_t)h * 2 + half) * n_sub * dh;
+        if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+        else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+        else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+        else mfma_scores<NT, 8>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+      } else {
+        const float* xcol = static_cast<const float*>(is_q ? a.qp : a.kp) +
+                            ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
+        const float* Cf =
+            static_cast<const float*>(a.subkeys) + ((int64_t)h * 2 + half) * n_sub * dh;
+        valu_scores<NT>(xcol, Cf, n_sub, dh, hw, hl, sc);
+      }
 
-    // ---- 2. stage 1: threshold over all waves, pack, sort -----------------
-    uint32_t o[NT][4];
-    float sum = 0.f, sq = 0.f;
-    uint32_t omax = 0u;
+      // ---- 2. stage 1: threshold over all waves, pack, sort -----------------
+      uint32_t o[NT][4];
+      float sum = 0.f, sq = 0.f;
+      uint32_t omax = 0u;
 #pragma unroll
-    for (int j = 0; j < NT; j++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
+      for (int j = 0; j < NT; j++) {
         const bool valid = 16 * (hw + kWaves * j) < n_sub;  // whole tiles
-        const float s = sc[j][r];
-        o[j][r] = valid ? ord32(s) : 0u;
-        sum += valid ? s : 0.f;
-        sq += valid ? s * s : 0.f;
-        omax = o[j][r] > omax ? o[j][r] : omax;
-      }
-    sum += xor_shuffle(sum, 16, hl);
-    sq += xor_shuffle(sq, 16, hl);
-    omax = max(omax, xor_shuffle(omax, 16, hl));
-    sum += xor_shuffle(sum, 32, hl);
-    sq += xor_shuffle(sq, 32, hl);
-    omax = max(omax, xor_shuffle(omax, 32, hl));
-    if (kq == 0) {
-      s_stat[hw][tl] = make_float2(sum, sq);
-      s_max[hw][tl] = omax;
-    }
-    __syncthreads();
-    sum = 0.f, sq = 0.f, omax = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-      const float2 v = s_stat[w][tl];
-      sum += v.x;
-      sq += v.y;
-      omax = max(omax, s_max[w][tl]);
-    }
-    const float mean = sum / n_sub;
-    const float sd = sqrtf(fmaxf(sq / n_sub - mean * mean, 0.f));
-    uint64_t lo = 0ull, hi = ((uint64_t)omax + 1ull) << 32;
-    const uint64_t guess = (uint64_t)ord32(mean + zc * sd) << 32;
-    uint64_t t = (guess > lo && guess < hi) ? guess : lo + (hi - lo) / 2;
-    int it = 0, own = 0;
-    for (;;) {
-      // keys are rebuilt from o in every round, not kept live across rounds
-#pragma unroll
-      for (int j = 0; j < NT; j++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) asm volatile("" : "+v"(o[j][r]));
-      own = count_own<NT>(o, base_id, t);
-      int ws = own + (int)xor_shuffle((uint32_t)own, 16, hl);
-      ws += (int)xor_shuffle((uint32_t)ws, 32, hl);
-      if (kq == 0) s_cnt[it & 1][hw][tl] = ws;
-      __syncthreads();
-      int tot = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; w++) tot += s_cnt[it & 1][w][tl];
-      const bool ok = !col_ok || (tot >= kc && tot <= capc);
-      if (__ballot(!ok) == 0ull || it >= 127) break;  // same decision in every wave
-      if (!ok) {
-        if (tot < kc) hi = t;
-        else lo = t;
-        t = hi - lo <= 1 ? lo : lo + (hi - lo) / 2;
-      }
-      it++;
-    }
-    const int fin = it & 1;
-    // pack this lane's keys >= t behind those of earlier waves and lanes
-    int pos = 0;
-    for (int w = 0; w < hw; w++) pos += s_cnt[fin][w][tl];
-    {
-      const int x16 = (int)xor_shuffle((uint32_t)own, 16, hl);  // kq ^ 1
-      const int x32 = (int)xor_shuffle((uint32_t)own, 32, hl);  // kq ^ 2
-      const int x48 = (int)xor_shuffle((uint32_t)x16, 32, hl);  // kq ^ 3
-      pos += kq == 0 ? 0 : kq == 1 ? x16 : kq == 2 ? x32 + x48 : x16 + x32 + x48;
-    }
-    if (col_ok) {
-      uint64_t* cb = cand + tl * L.capmax;
-#pragma unroll
-      for (int j = 0; j < NT; j++)
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const uint64_t kk = ((uint64_t)o[j][r] << 32) |
-                              (uint64_t)(0xffffffffu - (base_id + kWaves * 16 * j + r));
-          if (o[j][r] != 0u && kk >= t && pos < L.capmax) cb[pos++] = kk;
+          const float s = sc[j][r];
+          o[j][r] = valid ? ord32(s) : 0u;
+          sum += valid ? s : 0.f;
+          sq += valid ? s * s : 0.f;
+          omax = o[j][r] > omax ? o[j][r] : omax;
         }
-    }
-    __syncthreads();
-    // one wave per column sorts: wave w owns the key and query columns of token t0 + w
-    if (t0 + hw < a.T) {
+      }
+      sum += xor_shuffle(sum, 16, hl);
+      sq += xor_shuffle(sq, 16, hl);
+      omax = max(omax, xor_shuffle(omax, 16, hl));
+      sum += xor_shuffle(sum, 32, hl);
+      sq += xor_shuffle(sq, 32, hl);
+      omax = max(omax, xor_shuffle(omax, 32, hl));
+      if (kq == 0) {
+        s_stat[hw][tl] = make_float2(sum, sq);
+        s_max[hw][tl] = omax;
+      }
+      __syncthreads();
+      sum = 0.f, sq = 0.f, omax = 0u;
 #pragma unroll
-      for (int q = 0; q < 2; q++) {
-        const int cc = hw + q * kTT;
-        const int k = q ? a.R : a.W;
-        int c = 0;
+      for (int w = 0; w < kWaves; w++) {
+        const float2 v = s_stat[w][tl];
+        sum += v.x;
+        sq += v.y;
+        omax = max(omax, s_max[w][tl]);
+      }
+      const float mean = sum / n_sub;
+      const float sd = sqrtf(fmaxf(sq / n_sub - mean * mean, 0.f));
+      uint64_t lo = 0ull, hi = ((uint64_t)omax + 1ull) << 32;
+      const uint64_t guess = (uint64_t)ord32(mean + zc * sd) << 32;
+      uint64_t t = (guess > lo && guess < hi) ? guess : lo + (hi - lo) / 2;
+      int it = 0, own = 0;
+      for (;;) {
+        // keys are rebuilt from o in every round, not kept live across rounds
 #pragma unroll
-        for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
-        c = min(c, L.capmax);
-        float* ols = ls + (half * kCols + cc) * m;
-        int32_t* oli = li + (half * kCols + cc) * m;
-        sort_emit(cand + cc * L.capmax, c, k, hl, [&](int r, uint64_t kk) {
-          ols[r] = key_score(kk);
-          oli[r] = (int32_t)key_id(kk);
-        });
-        wave_lds_sync();
+        for (int j = 0; j < NT; j++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) asm volatile("" : "+v"(o[j][r]));
+        own = count_own<NT>(o, base_id, t);
+        int ws = own + (int)xor_shuffle((uint32_t)own, 16, hl);
+        ws += (int)xor_shuffle((uint32_t)ws, 32, hl);
+        if (kq == 0) s_cnt[it & 1][hw][tl] = ws;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) tot += s_cnt[it & 1][w][tl];
+        const bool ok = !col_ok || (tot >= kc && tot <= capc);
+        if (__ballot(!ok) == 0ull || it >= 127) break;  // same decision in every wave
+        if (!ok) {
+          if (tot < kc) hi = t;
+          else lo = t;
+          t = hi - lo <= 1 ? lo : lo + (hi - lo) / 2;
+        }
+        it++;
+      }
+      const int fin = it & 1;
+      // pack this lane's keys >= t behind those of earlier waves and lanes
+      int pos = 0;
+      for (int w = 0; w < hw; w++) pos += s_cnt[fin][w][tl];
+      {
+        const int x16 = (int)xor_shuffle((uint32_t)own, 16, hl);  // kq ^ 1
+        const int x32 = (int)xor_shuffle((uint32_t)own, 32, hl);  // kq ^ 2
+        const int x48 = (int)xor_shuffle((uint32_t)x16, 32, hl);  // kq ^ 3
+        pos += kq == 0 ? 0 : kq == 1 ? x16 : kq == 2 ? x32 + x48 : x16 + x32 + x48;
+      }
+      if (col_ok) {
+        uint64_t* cb = cand + (tl * 2 + half) * cm;
+        const uint32_t th = (uint32_t)(t >> 32), tlo = (uint32_t)t;
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const uint32_t ov = o[j][r];
+            const uint32_t lid = 0xffffffffu - (base_id + kWaves * 16 * j + r);
+            if ((ov > th || (ov == th && lid >= tlo)) && pos < cm)
+              cb[pos++] = ((uint64_t)ov << 32) | lid;
+          }
+      }
+      __syncthreads();
+      // one wave per column sorts: wave w owns the key and query columns of
+      // token t0 + w; the rank-ordered list of half h goes to [h*m, h*m + k)
+      // of the column's block (in place for h = 0: read before written)
+      if (t0 + hw < a.T) {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+          const int cc = hw + q * kTT;
+          const int k = q ? a.R : a.W;
+          int c = 0;
+#pragma unroll
+          for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
+          c = min(c, cm);
+          uint64_t* lst = cand + cc * 2 * cm + half * m;
+          sort_emit(cand + (cc * 2 + half) * cm, c, k, hl, [&](int r, uint64_t kk) { lst[r] = kk; });
+        }
       }
     }
-  }
 
-  // ---- 3. stage 2: this wave's two columns (lists written by this wave) ----
-  __syncthreads();  // grid rows filled by every wave
-  const int n_sub = a.n_sub;
-  const int tw = t0 + wave;
-  if (tw < a.T) {
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const int cc = wave + q * kTT;
-      const int k = q ? a.R : a.W;
-      const bool own_grid = q && L.gR;
-      stage2<NPL2>(ls + cc * m, li + cc * m, ls + (kCols + cc) * m, li + (kCols + cc) * m, k, k,
-                   n_sub, own_grid ? grid + L.gW : grid, own_grid ? L.gR : L.gW,
-                   cand + cc * L.capmax, lane,
-                   (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,
-                   (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
+    // ---- 3. stage 2: this wave's two columns (lists written by this wave) ----
+    wave_lds_sync();
+    const int tw = t0 + wave;
+    if (tw < a.T) {
+      for (int q = 0; q < 2; q++) {
+        const int cc = wave + q * kTT;
+        const int k = q ? a.R : a.W;
+        const bool own_grid = q && L.gR;
+        uint64_t* blk = cand + cc * 2 * cm;
+        stage2<NPL2>(blk, blk + m, k, k, a.n_sub, own_grid ? grid + L.gW : grid,
+                     own_grid ? L.gR : L.gW, blk + 2 * m, lane,
+                     (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,
+                     (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
+      }
     }
   }
 }
@@ -710,8 +759,13 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
-  dim3 grid((a.T + kTT - 1) / kTT, a.S);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), L.total, stream, a, guess_z(a.W, a.n_sub),
+  // token tiles per workgroup: up to 4 (one grid build serves them all)
+  // while the launch still has at least 2048 workgroups
+  const int ntiles = (a.T + kTT - 1) / kTT;
+  int per = 1;
+  while (per < 4 && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
+  dim3 grid((ntiles + per - 1) / per, a.S);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), L.total, stream, a, per, guess_z(a.W, a.n_sub),
                      guess_z(a.R, a.n_sub));
   return hipGetLastError();
 }
@@ -723,10 +777,9 @@ template <int NT>
 hipError_t launch_score_t(const ScoreArgs& a, bool bf16, int npl2, hipStream_t stream) {
 #define SDM_SCORE_CASE(M_)                                                      \
   if (npl2 <= M_) return bf16 ? launch_t<true, NT, M_>(a, stream) : launch_t<false, NT, M_>(a, stream);
-  SDM_SCORE_CASE(4)
-  SDM_SCORE_CASE(8)
-  SDM_SCORE_CASE(12)
-  SDM_SCORE_CASE(16)
+  SDM_SCORE_CASE(2)
+  SDM_SCORE_CASE(5)
+  SDM_SCORE_CASE(11)
 #undef SDM_SCORE_CASE
   return hipErrorInvalidValue;
 }
