@@ -144,8 +144,10 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int lane) {
           const int i = lane * E + r;
           const bool lower = (i & j) == 0;
           const bool desc = (i & s) == 0;
-          const bool keep_max = lower == desc;
-          v[r] = keep_max ? (o > v[r] ? o : v[r]) : (o < v[r] ? o : v[r]);
+          // keep the larger of the pair in the lower slot of a descending run
+          // (and in the upper slot of an ascending one); equal keys are equal
+          // values, so one compare decides
+          v[r] = ((o > v[r]) == (lower == desc)) ? o : v[r];
         }
       } else {
 #pragma unroll
@@ -154,7 +156,7 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int lane) {
             const int i = lane * E + r;
             const bool desc = (i & s) == 0;
             const uint64_t p = v[r], q = v[r | j];
-            const bool swap = desc ? (q > p) : (q < p);
+            const bool swap = (q > p) == desc;  // equal keys: swapping changes nothing
             v[r] = swap ? q : p;
             v[r | j] = swap ? p : q;
           }
@@ -241,18 +243,19 @@ namespace {
 
 // Half scores of the 16 columns against this wave's sub-key tiles
 // i0 = 16*(wave + 8*j), j < NT: D[sub-key][column] = sum_e C[sub-key][e] *
-// x[column][e] on v_mfma_f32_16x16x32_bf16.  n_sub is a multiple of 16, so a
-// tile is wholly inside the table or wholly outside (skipped, scores 0).
-// Sub-key rows are read through a buffer resource per tile whose range ends
-// at the table's end: one offset register serves every tile, and the reads
-// past a row's dh elements (dh not a multiple of 32) meet a zero B fragment
-// or, past the table, read as zero.  xcol points at this lane's column half
-// (any valid row when !col_ok).
+// x[column][e] on v_mfma_f32_16x16x32_bf16.  Sub-key rows are read through a
+// buffer resource whose range ends at the table's end, so rows of tiles past
+// n_sub (and the tail past dh when dh is not a multiple of 32) read as zero
+// or meet a zero B fragment; there is no branch, and each batch's loads are
+// all in flight before its first MFMA.  n_sub is a multiple of 16: such tiles
+// are wholly outside and their scores are discarded by the caller.  xcol
+// points at this lane's column half (any valid row when !col_ok).
 template <int NT, int KS>
 __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, const uint16_t* Cb,
                                             int n_sub, int dh, int wave, int lane,
                                             float (&sc)[NT][4]) {
   constexpr int TB = 8 / KS > 0 ? 8 / KS : 1;  // sub-key tiles loaded together
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int tl = lane & 15;  // sub-key row of the A tile, column of the B tile
   const int kq = lane >> 4;  // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
@@ -262,34 +265,28 @@ __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, c
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(xcol + min(d0, dh - 8));
     bfrag[ks] = (col_ok && d0 < dh) ? v : bf16x8{};
   }
-  const int voff = (tl * dh + kq * 8) * 2;  // bytes within a tile
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Cb, (short)0, n_sub * dh * 2, 0x00020000);
+  const int voff = ((16 * wave + tl) * dh + kq * 8) * 2;  // bytes, tile j = 0
+  const int tstep = kWaves * 16 * dh * 2;                 // bytes from tile j to j + 1
 #pragma unroll
   for (int j0 = 0; j0 < NT; j0 += TB) {
-    bf16x8 af[TB][KS];
+    u32x4 af[TB][KS];
+#pragma unroll
+    for (int t = 0; t < TB; t++)
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        if (j0 + t < NT)
+          af[t][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (j0 + t) * tstep + ks * 64,
+                                                            0, 0);
 #pragma unroll
     for (int t = 0; t < TB; t++) {
-      const int i0 = 16 * (wave + kWaves * (j0 + t));
-      if (j0 + t < NT && i0 < n_sub) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(Cb + (int64_t)i0 * dh), (short)0, (n_sub - i0) * dh * 2, 0x00020000);
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + ks * 64, 0, 0);
-          af[t][ks] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < TB; t++) {
-      const int i0 = 16 * (wave + kWaves * (j0 + t));
       if (j0 + t < NT) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (i0 < n_sub) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ks++)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t][ks], bfrag[ks], acc, 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ks++)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[t][ks]),
+                                                        bfrag[ks], acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; r++) sc[j0 + t][r] = acc[r];
       }

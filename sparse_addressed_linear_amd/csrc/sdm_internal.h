@@ -44,10 +44,24 @@ __device__ __forceinline__ float xor_shuffle(float v, int m, int lane) {
   return __uint_as_float(xor_shuffle(__float_as_uint(v), m, lane));
 }
 
+// 64-bit form: the DPP moves write both halves of the destination pair
+// directly (no repacking moves).
 __device__ __forceinline__ uint64_t xor_shuffle(uint64_t v, int m, int lane) {
-  const uint32_t lo = xor_shuffle((uint32_t)v, m, lane);
-  const uint32_t hi = xor_shuffle((uint32_t)(v >> 32), m, lane);
-  return ((uint64_t)hi << 32) | lo;
+  switch (m) {
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const uint64_t up = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);
+      const uint64_t dn = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);
+      return (lane & 4) ? dn : up;
+    }
+    case 8: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+    default: {
+      const uint32_t lo = xor_shuffle((uint32_t)v, m, lane);
+      const uint32_t hi = xor_shuffle((uint32_t)(v >> 32), m, lane);
+      return ((uint64_t)hi << 32) | lo;
+    }
+  }
 }
 
 struct ScanArgs {
