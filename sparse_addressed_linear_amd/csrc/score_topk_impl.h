@@ -214,7 +214,7 @@ __device__ __forceinline__ int compact_ge(const uint64_t (&key)[NPL], uint64_t t
 // then, once sorted, the two rank-ordered lists at [0, m) and [m, 2m) and
 // stage 2's scratch at [2m, 2m + capmax) (capmax >= 2m).
 struct ScoreSmem {
-  size_t cand, grid, rowoff, total;
+  size_t cand, grid, rowoff, dump, total;
   int m, capmax, gW, gR;  // list length, candidate stride, grid sizes
 };
 
@@ -235,6 +235,8 @@ __host__ __device__ inline ScoreSmem score_smem(int W, int R) {
   s.cand = o;   o += (size_t)kCols * 2 * s.capmax * 8;
   s.grid = o;   o += (size_t)(s.gW + s.gR) * 4;  // (ra << 16) | rb, W grid then R grid
   s.rowoff = o; o += (size_t)2 * (s.m + 1) * 4;
+  o = (o + 15) & ~(size_t)15;
+  s.dump = o;   o += (size_t)kWaves * 64 * 8;  // one slot per lane for discarded stores
   s.total = o;
   return s;
 }
@@ -347,16 +349,16 @@ __device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int la
 #pragma unroll
   for (int r = 0; r < E; r++) {
     const int p = lane * E + r;
-    e[r] = p < k ? expf(key_score(v[r]) - top) : 0.f;
+    e[r] = p < k ? __expf(key_score(v[r]) - top) : 0.f;
     z += e[r];
   }
-  z = wave_sum(z);
+  const float iz = 1.0f / wave_sum(z);
 #pragma unroll
   for (int r = 0; r < E; r++) {
     const int p = lane * E + r;
     if (p < k) {
       dst_i[p] = (int32_t)key_id(v[r]);
-      dst_w[p] = e[r] / z;
+      dst_w[p] = e[r] * iz;
     }
   }
 }
@@ -407,9 +409,10 @@ __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, const 
 // softmax weights.  buf holds cap_for(k) keys of scratch.
 template <int NPL2>
 __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, int m, int k,
-                                       int n_sub, const uint32_t* grid, int G, uint64_t* buf,
-                                       int lane, int32_t* dst_i, float* dst_w) {
+                                       int n_sub, const uint32_t* grid, int G, float z,
+                                       uint64_t* buf, int lane, int32_t* dst_i, float* dst_w) {
   uint64_t key[NPL2];
+  float sum = 0.f, sq = 0.f;
 #pragma unroll
   for (int j = 0; j < NPL2; j++) {
     const int c = j * 64 + lane;
@@ -417,7 +420,10 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
     if (c < G) {
       const uint32_t ab = grid[c];
       const uint64_t a1 = L1[ab >> 16], a2 = L2[ab & 0xffff];
-      key[j] = make_key(key_score(a1) + key_score(a2), key_id(a1) * (uint32_t)n_sub + key_id(a2));
+      const float s = key_score(a1) + key_score(a2);
+      key[j] = make_key(s, key_id(a1) * (uint32_t)n_sub + key_id(a2));
+      sum += s;
+      sq += s * s;
     }
   }
   const int cap = cap_for(k);
@@ -425,17 +431,13 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
 #pragma unroll
   for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
   mx = wave_max64(mx);
-  // first threshold: for any rank ra the rectangle [0..ra] x [0..cb] with
-  // cb = ceil(k/(ra+1)) - 1 holds at least k sums, all at least its corner's,
-  // so the best corner is a lower bound of the k-th sum
-  uint64_t lb = 0ull;
-  for (int ra = lane; ra < m; ra += 64) {
-    const int cb = (k + ra) / (ra + 1) - 1;
-    const uint64_t kk = (uint64_t)ord32(key_score(L1[ra]) + key_score(L2[cb])) << 32;
-    lb = kk > lb ? kk : lb;
-  }
-  lb = wave_max64(lb);
-  const uint64_t t = find_threshold(key, k, cap, lb, 0ull, mx + 1ull);
+  // first threshold from the mean and spread of the G sums
+  sum = wave_sum(sum);
+  sq = wave_sum(sq);
+  const float mean = sum / G;
+  const float sd = sqrtf(fmaxf(sq / G - mean * mean, 0.f));
+  const uint64_t guess = (uint64_t)ord32(mean + z * sd) << 32;
+  const uint64_t t = find_threshold(key, k, cap, guess, 0ull, mx + 1ull);
   const int c = compact_ge(key, t, buf, lane);
   wave_lds_sync();
   bool done;
@@ -485,13 +487,13 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
   sort_emit(buf, base, k, lane, [&](int r, uint64_t kk) { buf[r] = kk; });
   wave_lds_sync();
   const float top = key_score(buf[0]);
-  float z = 0.f;
-  for (int r = lane; r < k; r += 64) z += expf(key_score(buf[r]) - top);
-  z = wave_sum(z);
+  float zs = 0.f;
+  for (int r = lane; r < k; r += 64) zs += __expf(key_score(buf[r]) - top);
+  const float iz = 1.0f / wave_sum(zs);
   for (int r = lane; r < k; r += 64) {
     const uint64_t kk = buf[r];
     dst_i[r] = (int32_t)key_id(kk);
-    dst_w[r] = expf(key_score(kk) - top) / z;
+    dst_w[r] = __expf(key_score(kk) - top) * iz;
   }
 }
 
@@ -519,9 +521,15 @@ __device__ __forceinline__ void grid_fill(int k, const int32_t* rowoff, uint32_t
   }
 }
 
+// First-guess quantiles: a Gaussian model puts about 1.4k of the n stage-1
+// scores (of the G stage-2 sums) above mean + z * sd.
+struct ScoreZ {
+  float w1, r1, w2, r2;
+};
+
 template <bool BF16, int NT, int NPL2>
 __global__ void __launch_bounds__(kThreads, 4)
-    sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, float zW, float zR) {
+    sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, ScoreZ z) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float2 s_stat[kWaves][kCols];    // per wave: sum, sum of squares
   __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
@@ -563,7 +571,7 @@ __global__ void __launch_bounds__(kThreads, 4)
       const bool col_ok = tok < a.T;
       const int kc = is_q ? a.R : a.W;
       const int capc = cap_for(kc);
-      const float zc = is_q ? zR : zW;
+      const float zc = is_q ? z.r1 : z.w1;
       const uint32_t base_id = 16u * hw + 4u * kq;  // sub-key id of this lane's first score
 
       // ---- 1. half scores ---------------------------------------------------
@@ -659,18 +667,38 @@ __global__ void __launch_bounds__(kThreads, 4)
         const int x48 = (int)xor_shuffle((uint32_t)x16, 32, hl);  // kq ^ 3
         pos += kq == 0 ? 0 : kq == 1 ? x16 : kq == 2 ? x32 + x48 : x16 + x32 + x48;
       }
-      if (col_ok) {
+      {
+        // every position stores: kept keys to the column's block, the others
+        // to this lane's own discard slot (no branches, no exec-mask churn)
         uint64_t* cb = cand + (tl * 2 + half) * cm;
+        uint64_t* dump = reinterpret_cast<uint64_t*>(smem + L.dump) + hw * 64 + hl;
         const uint32_t th = (uint32_t)(t >> 32), tlo = (uint32_t)t;
+        const int lim = col_ok ? cm : 0;
+        if (tlo == 0u && __ballot(tlo != 0u) == 0ull) {
+          // threshold on the score part alone (the usual case)
 #pragma unroll
-        for (int j = 0; j < NT; j++)
+          for (int j = 0; j < NT; j++)
 #pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const uint32_t ov = o[j][r];
-            const uint32_t lid = 0xffffffffu - (base_id + kWaves * 16 * j + r);
-            if ((ov > th || (ov == th && lid >= tlo)) && pos < cm)
-              cb[pos++] = ((uint64_t)ov << 32) | lid;
-          }
+            for (int r = 0; r < 4; r++) {
+              const uint32_t ov = o[j][r];
+              const bool keep = ov >= th && pos < lim;
+              uint64_t* dst = keep ? cb + pos : dump;
+              *dst = ((uint64_t)ov << 32) | (0xffffffffu - (base_id + kWaves * 16 * j + r));
+              pos += keep ? 1 : 0;
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NT; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const uint32_t ov = o[j][r];
+              const uint32_t lid = 0xffffffffu - (base_id + kWaves * 16 * j + r);
+              const bool keep = (ov > th || (ov == th && lid >= tlo)) && pos < lim;
+              uint64_t* dst = keep ? cb + pos : dump;
+              *dst = ((uint64_t)ov << 32) | lid;
+              pos += keep ? 1 : 0;
+            }
+        }
       }
       __syncthreads();
       // one wave per column sorts: wave w owns the key and query columns of
@@ -701,7 +729,7 @@ __global__ void __launch_bounds__(kThreads, 4)
         const bool own_grid = q && L.gR;
         uint64_t* blk = cand + cc * 2 * cm;
         stage2<NPL2>(blk, blk + m, k, k, a.n_sub, own_grid ? grid + L.gW : grid,
-                     own_grid ? L.gR : L.gW, blk + 2 * m, lane,
+                     own_grid ? L.gR : L.gW, q ? z.r2 : z.w2, blk + 2 * m, lane,
                      (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,
                      (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
       }
@@ -745,7 +773,7 @@ static inline double norm_quantile(double p) {
 // threshold z such that about 1.4*k of n Gaussian scores lie above mean + z*sd
 static inline float guess_z(int k, int n) {
   double f = 1.4 * k / n;
-  if (f > 0.9) f = 0.9;
+  if (f > 0.95) f = 0.95;
   return (float)norm_quantile(1.0 - f);
 }
 
@@ -762,8 +790,9 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   int per = 1;
   while (per < 4 && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
   dim3 grid((ntiles + per - 1) / per, a.S);
-  hipLaunchKernelGGL(k, grid, dim3(kThreads), L.total, stream, a, per, guess_z(a.W, a.n_sub),
-                     guess_z(a.R, a.n_sub));
+  const ScoreZ z{guess_z(a.W, a.n_sub), guess_z(a.R, a.n_sub), guess_z(a.W, pruned_grid_size(a.W)),
+                 guess_z(a.R, pruned_grid_size(a.R))};
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), L.total, stream, a, per, z);
   return hipGetLastError();
 }
 
