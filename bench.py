@@ -43,6 +43,22 @@ def score_bytes_per_token(wl):
     return 2 * wl.d_k * e + 2 * (wl.W + wl.R) * 8 + wl.d_v * e + 8 + wl.d_v * 4
 
 
+def measured_scan_traffic(wl):
+    """HBM bytes per scan launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters (copy-calibrated), or None when they were taken on
+    another workload or the scan sources have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"scan_{wl.name}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "sparse_addressed_linear_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("scan.hip", "sdm_internal.h"))
+    if rec.get("scan_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(wl, x, n_streams):
     """Oracle (single thread) on the first n_streams streams, all tokens."""
     import oracle
@@ -97,6 +113,9 @@ def main():
     ap.add_argument("--config", default="large", choices=["tiny", "mid", "large", "long", "gdn"])
     ap.add_argument("--cpu-streams", type=int, default=None,
                     help="streams in the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
+                    help="only run 3 plain device copies of GIB GiB (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -112,6 +131,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe is not None:
+        n = int(args.copy_probe * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "launches": 3}), flush=True)
+        return
     sdm.lib()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.config]
@@ -120,7 +149,9 @@ def main():
           flush=True)
     x = synth.make_inputs(wl, device=dev)
     dense = wl.dense
-    n_cpu = args.cpu_streams if args.cpu_streams is not None else (2 if dense else 8)
+    # oracle sample sized for roughly 10-20 s of single-threaded CPU work
+    default_cpu = {"tiny": 1, "mid": 16, "large": 24, "long": 1, "gdn": 2}[wl.name]
+    n_cpu = args.cpu_streams if args.cpu_streams is not None else default_cpu
     n_cpu = min(n_cpu, wl.streams)
     if not dense and n_cpu:
         # initial tables of the CPU sample, taken before the GPU steps modify M
@@ -192,7 +223,7 @@ def main():
         achieved = sbytes / (ms_scan * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_scan_traffic(wl),
                 "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
         allb = stream_tokens * (scan_bytes_per_token(wl) + score_bytes_per_token(wl))
         kernels = {"score_topk_ms": round(ms_score, 4), "scan_ms": round(ms_scan, 4),

@@ -122,10 +122,10 @@ int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, con
  * and writes outside the stream's table).  Results are deterministic (the
  * read sums use a fixed order).  Scanning [0,T1) and then [T1,T) with the same
  * M leaves a table bit-identical to one scan of [0,T), and bit-identical
- * outputs as well, except for tokens whose write plus read slots overflow the
- * kernel's per-wave capacity (more than 128 of them in one slot partition,
- * 256 when d_v is not a multiple of 32), whose outputs then agree to fp32
- * rounding.
+ * outputs as well, except for tokens whose write plus read slots in one slot
+ * partition exceed what a wave holds in registers (between 64 and 256 events,
+ * sized from W, R and the partition count for a few standard deviations above
+ * the mean), whose outputs then agree to fp32 rounding.
  * Two calls that overlap on one device must not share M, out or workspace.
  * Kernel limits (else SDM_ERR_UNSUPPORTED): d_v a multiple of 16 and <= 512,
  * W, R <= 256.
