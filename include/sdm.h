@@ -81,6 +81,10 @@ typedef struct {
  *   wwt      [B][H][T][W]  fp32    out: write weights
  *   ridx     [B][H][T][R]  int32   out: read slots, rank order
  *   rwt      [B][H][T][R]  fp32    out: read weights
+ *   workspace                       device scratch of at least
+ *                                   sdm_score_topk_workspace_size(dims, in_dtype)
+ *                                   bytes (may be NULL when that size is 0);
+ *                                   its contents on entry do not matter.
  *
  * Scores are accumulated in fp32 (bf16 products are exact in fp32).
  * Kernel limits (else SDM_ERR_UNSUPPORTED): n_sub a multiple of 16 and
@@ -89,7 +93,13 @@ typedef struct {
  */
 int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, const void* kp,
                    const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
-                   void* stream);
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sdm_score_topk needs for these sizes and input
+ * type (0 when none, or when the sizes are invalid).  Pure host function.
+ * With bf16 inputs the call first copies the sub-key tables there in the
+ * order the matrix cores read them (about n_sub*d_k*2 bytes per head). */
+size_t sdm_score_topk_workspace_size(const sdm_dims* dims, sdm_dtype in_dtype);
 
 /*
  * sdm_scan -- sparse gated-delta write and sparse read over the memory table

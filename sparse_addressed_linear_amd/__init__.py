@@ -14,8 +14,8 @@ import os
 
 import torch
 
-__all__ = ["lib", "score_topk", "scan", "gdn_scan", "scan_workspace_size", "SdmError",
-           "LIB_PATH", "Dims"]
+__all__ = ["lib", "score_topk", "score_topk_workspace_size", "scan", "gdn_scan",
+           "scan_workspace_size", "SdmError", "LIB_PATH", "Dims"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdm.so")
 
@@ -23,8 +23,8 @@ SDM_F32, SDM_BF16 = 0, 1
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE",
           4: "SDM_ERR_UNSUPPORTED", 5: "SDM_ERR_ALIGN", 6: "SDM_ERR_HIP",
           7: "SDM_ERR_WORKSPACE"}
-EXPORTS = ("sdm_score_topk", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
-           "sdm_status_str", "sdm_version")
+EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_scan",
+           "sdm_scan_workspace_size", "sdm_gdn_scan", "sdm_status_str", "sdm_version")
 
 
 class SdmError(RuntimeError):
@@ -51,8 +51,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         PD = ctypes.POINTER(Dims)
-        L.sdm_score_topk.argtypes = [PD, I32, P, P, P, P, P, P, P, P]
+        L.sdm_score_topk.argtypes = [PD, I32, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_score_topk.restype = ctypes.c_int
+        L.sdm_score_topk_workspace_size.argtypes = [PD, I32]
+        L.sdm_score_topk_workspace_size.restype = SZ
         L.sdm_scan.argtypes = [PD, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_scan.restype = ctypes.c_int
         L.sdm_scan_workspace_size.argtypes = [PD]
@@ -101,10 +103,11 @@ def _check(fn, rc):
         raise SdmError(fn, rc)
 
 
-def score_topk(qp, kp, subkeys, W, R, out=None, stream=None):
+def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None):
     """Product-key addressing.  qp, kp: [B,H,T,d_k]; subkeys: [H,2,n_sub,d_k/2]
     (all fp32 or all bf16).  Returns (widx, wwt, ridx, rwt): [B,H,T,W] int32,
-    fp32 and [B,H,T,R] int32, fp32, in rank order."""
+    fp32 and [B,H,T,R] int32, fp32, in rank order.  ``workspace`` (uint8 device
+    tensor) is allocated here when not given or too small."""
     B, H, T, d_k = qp.shape
     if kp.shape != qp.shape or subkeys.dim() != 4 or subkeys.shape[0] != H or \
             subkeys.shape[1] != 2 or subkeys.shape[3] * 2 != d_k:
@@ -119,12 +122,22 @@ def score_topk(qp, kp, subkeys, W, R, out=None, stream=None):
                torch.empty((B, H, T, R), dtype=torch.float32, device=dev))
     widx, wwt, ridx, rwt = out
     d = Dims(B, H, T, d_k, n_sub, 1, W, R)
+    need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     rc = lib().sdm_score_topk(ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"),
                               _dev(subkeys, "subkeys"), _dev(widx, "widx", torch.int32),
                               _dev(wwt, "wwt", torch.float32), _dev(ridx, "ridx", torch.int32),
-                              _dev(rwt, "rwt", torch.float32), _stream(stream))
+                              _dev(rwt, "rwt", torch.float32), wsp, ctypes.c_size_t(need),
+                              _stream(stream))
     _check("sdm_score_topk", rc)
     return widx, wwt, ridx, rwt
+
+
+def score_topk_workspace_size(B, H, T, d_k, n_sub, W, R, bf16=True):
+    d = Dims(B, H, T, d_k, n_sub, 1, W, R)
+    return int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), SDM_BF16 if bf16 else SDM_F32))
 
 
 def scan_workspace_size(B, H, T, N, d_v, W, R):

@@ -245,20 +245,20 @@ namespace {
 
 // Half scores of the 16 columns against this wave's sub-key tiles
 // i0 = 16*(wave + 8*j), j < NT: D[sub-key][column] = sum_e C[sub-key][e] *
-// x[column][e] on v_mfma_f32_16x16x32_bf16.  Sub-key rows are read through a
-// buffer resource whose range ends at the table's end, so rows of tiles past
-// n_sub (and the tail past dh when dh is not a multiple of 32) read as zero
-// or meet a zero B fragment; there is no branch, and each batch's loads are
-// all in flight before its first MFMA.  n_sub is a multiple of 16: such tiles
-// are wholly outside and their scores are discarded by the caller.  xcol
-// points at this lane's column half (any valid row when !col_ok).
+// x[column][e] on v_mfma_f32_16x16x32_bf16.  The A fragments come from the
+// packed copy of this head-half's sub-keys ([tile][K step][lane] x 16 bytes,
+// dh padded with zeros to a multiple of 32), so each load instruction reads
+// 1 KB contiguous; tiles past n_sub fall outside the buffer resource and read
+// as zero (n_sub is a multiple of 16, so such tiles are wholly outside and
+// their scores are discarded by the caller).  There is no branch, and each
+// batch's loads are all in flight before its first MFMA.  xcol points at this
+// lane's column half (any valid row when !col_ok).
 template <int NT, int KS>
-__device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, const uint16_t* Cb,
-                                            int n_sub, int dh, int wave, int lane,
-                                            float (&sc)[NT][4]) {
+__device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok,
+                                            const unsigned char* Pb, int n_tiles, int dh,
+                                            int wave, int lane, float (&sc)[NT][4]) {
   constexpr int TB = 8 / KS > 0 ? 8 / KS : 1;  // sub-key tiles loaded together
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const int tl = lane & 15;  // sub-key row of the A tile, column of the B tile
   const int kq = lane >> 4;  // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
 #pragma unroll
@@ -268,9 +268,9 @@ __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, c
     bfrag[ks] = (col_ok && d0 < dh) ? v : bf16x8{};
   }
   const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Cb, (short)0, n_sub * dh * 2, 0x00020000);
-  const int voff = ((16 * wave + tl) * dh + kq * 8) * 2;  // bytes, tile j = 0
-  const int tstep = kWaves * 16 * dh * 2;                 // bytes from tile j to j + 1
+      __builtin_amdgcn_make_buffer_rsrc((void*)Pb, (short)0, n_tiles * KS * 1024, 0x00020000);
+  const int voff = (wave * KS * 64 + lane) * 16;  // tile j = 0, K step 0
+  constexpr int tstep = kWaves * KS * 1024;       // bytes from tile j to j + 1
 #pragma unroll
   for (int j0 = 0; j0 < NT; j0 += TB) {
     u32x4 af[TB][KS];
@@ -279,8 +279,8 @@ __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok, c
 #pragma unroll
       for (int ks = 0; ks < KS; ks++)
         if (j0 + t < NT)
-          af[t][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (j0 + t) * tstep + ks * 64,
-                                                            0, 0);
+          af[t][ks] =
+              __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (j0 + t) * tstep + ks * 1024, 0, 0);
 #pragma unroll
     for (int t = 0; t < TB; t++) {
       if (j0 + t < NT) {
@@ -579,12 +579,14 @@ __global__ void __launch_bounds__(kThreads, 4)
       if (BF16) {
         const uint16_t* xcol = static_cast<const uint16_t*>(is_q ? a.qp : a.kp) +
                                ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
-        const uint16_t* Cb = static_cast<const uint16_t*>(a.subkeys) +
-                             ((int64_t)h * 2 + half) * n_sub * dh;
-        if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-        else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-        else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
-        else mfma_scores<NT, 8>(xcol, col_ok, Cb, n_sub, dh, hw, hl, sc);
+        const int n_tiles = n_sub / 16;
+        const int ksteps = (dh + 31) / 32;
+        const unsigned char* Pb = static_cast<const unsigned char*>(a.packed) +
+                                  ((int64_t)h * 2 + half) * n_tiles * ksteps * 1024;
+        if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else mfma_scores<NT, 8>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
       } else {
         const float* xcol = static_cast<const float*>(is_q ? a.qp : a.kp) +
                             ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;

@@ -34,9 +34,14 @@ bool valid_dtype(int t) { return t == SDM_F32 || t == SDM_BF16; }
 
 extern "C" {
 
+size_t sdm_score_topk_workspace_size(const sdm_dims* d, sdm_dtype in_dtype) {
+  if (!d || check_dims(d) != SDM_OK || !valid_dtype(in_dtype)) return 0;
+  return sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
+}
+
 int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
                    const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
-                   void* stream) {
+                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!d || !subkeys) return SDM_ERR_NULL;
   int rc = check_dims(d);
   if (rc) return rc;
@@ -52,7 +57,12 @@ int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const 
       !aligned16(wwt) || !aligned16(ridx) || !aligned16(rwt))
     return SDM_ERR_ALIGN;
   if (d->T == 0) return SDM_OK;
+  const size_t need =
+      sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SDM_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return SDM_ERR_ALIGN;
   sdm::ScoreArgs a{};
+  a.packed = workspace;
   a.qp = qp;
   a.kp = kp;
   a.subkeys = subkeys;

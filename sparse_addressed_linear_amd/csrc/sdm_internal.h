@@ -99,6 +99,7 @@ struct ScoreArgs {
   const void* qp;          // [S][T][d_k]
   const void* kp;
   const void* subkeys;     // [H][2][n_sub][dh]
+  void* packed;            // bf16: sub-key MFMA fragments (workspace)
   int32_t* widx;           // [S][T][W]
   float* wwt;
   int32_t* ridx;           // [S][T][R]
@@ -107,6 +108,7 @@ struct ScoreArgs {
 };
 
 hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream);
+size_t score_topk_workspace_bytes(int H, int n_sub, int d_k, bool bf16);
 
 struct GdnArgs {
   float* S;                // [S][d_v][d_k]

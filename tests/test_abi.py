@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
-        ["sdm_score_topk", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
-         "sdm_status_str", "sdm_version"])
+        ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_scan",
+         "sdm_scan_workspace_size", "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -52,17 +52,17 @@ def dims(**kw):
 P = ctypes.c_void_p(4096)  # aligned, never dereferenced: validation fails first
 
 
-def score(L, d, dt=1, ptr=P, null_at=None):
+def score(L, d, dt=1, ptr=P, null_at=None, ws=1 << 30, wsp=P):
     args = [ptr] * 7
     if null_at is not None:
         args[null_at] = ctypes.c_void_p(0)
-    return L.sdm_score_topk(ctypes.byref(d), dt, *args, None)
+    return L.sdm_score_topk(ctypes.byref(d), dt, *args, wsp, ctypes.c_size_t(ws), None)
 
 
 def test_score_topk_rejects(L):
     for i in range(7):
         assert score(L, dims(), null_at=i) == 1
-    assert L.sdm_score_topk(None, 1, *([P] * 7), None) == 1
+    assert L.sdm_score_topk(None, 1, *([P] * 7), P, ctypes.c_size_t(1 << 30), None) == 1
     assert score(L, dims(d_k=31)) == 2          # odd d_k
     assert score(L, dims(W=0)) == 2
     assert score(L, dims(W=1025)) == 2          # W > N
@@ -76,6 +76,19 @@ def test_score_topk_rejects(L):
     assert score(L, dims(), ptr=ctypes.c_void_p(4100)) == 5
 
 
+def test_score_topk_workspace_contract(L):
+    import sparse_addressed_linear_amd as sdm
+    d = dims(B=2, H=8, T=4096, d_k=128, n_sub=1024, W=64, R=64)
+    need = L.sdm_score_topk_workspace_size(ctypes.byref(d), 1)
+    # bf16: the packed sub-key fragments, 8 heads x 2 halves x 64 tiles x 2 K steps x 1 KB
+    assert need == 8 * 2 * 64 * 2 * 1024
+    assert L.sdm_score_topk_workspace_size(ctypes.byref(d), 0) == 0  # fp32 needs none
+    assert score(L, d, ws=need - 1) == 7
+    assert score(L, d, ws=need, wsp=ctypes.c_void_p(0)) == 7
+    assert score(L, d, ws=need, wsp=ctypes.c_void_p(4104)) == 5
+    assert sdm.score_topk_workspace_size(2, 8, 4096, 128, 1024, 64, 64) == need
+
+
 def scan(L, d, dt=0, ptr=P, ws=0, null_at=None):
     args = [ptr] * 9
     if null_at is not None:
@@ -86,7 +99,7 @@ def scan(L, d, dt=0, ptr=P, ws=0, null_at=None):
 def test_empty_sequence_accepts_null_token_tensors(L):
     z = ctypes.c_void_p(0)
     d = dims(T=0)
-    assert L.sdm_score_topk(ctypes.byref(d), 1, z, z, P, z, z, z, z, None) == 0
+    assert L.sdm_score_topk(ctypes.byref(d), 1, z, z, P, z, z, z, z, z, ctypes.c_size_t(0), None) == 0
     assert L.sdm_scan(ctypes.byref(d), 0, P, *([z] * 8), z, ctypes.c_size_t(0), None) == 0
     assert L.sdm_gdn_scan(1, 1, 0, 128, 128, 0, P, *([z] * 6), None) == 0
     assert L.sdm_scan(ctypes.byref(d), 0, z, *([z] * 8), z, ctypes.c_size_t(0), None) == 1
