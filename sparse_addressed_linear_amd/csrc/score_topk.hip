@@ -50,6 +50,7 @@ size_t score_topk_lds_bytes(int n_sub, int W, int R) {
 
 hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
+  if (bf16 && a.packed == nullptr) return hipErrorInvalidValue;  // the packed fragments' home
   if (bf16) {
     const int dh = a.d_k / 2;
     const int ksteps = (dh + 31) / 32;
