@@ -37,6 +37,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -189,6 +191,104 @@ __device__ __forceinline__ void sort_emit(uint64_t* buf, int c, int k, int lane,
   if (c <= 64) sort_emit_e<1>(buf, c, k, lane, emit);
   else if (c <= 128) sort_emit_e<2>(buf, c, k, lane, emit);
   else sort_emit_e<4>(buf, c, k, lane, emit);
+}
+
+// The same network on 32-bit keys.
+template <int E>
+__device__ __forceinline__ void bitonic_desc32(uint32_t (&v)[E], int lane) {
+#pragma unroll
+  for (int s = 2; s <= 64 * E; s <<= 1) {
+#pragma unroll
+    for (int j = s >> 1; j > 0; j >>= 1) {
+      if (j >= E) {
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+          const uint32_t o = xor_shuffle(v[r], j / E, lane);
+          const int i = lane * E + r;
+          const bool lower = (i & j) == 0;
+          const bool desc = (i & s) == 0;
+          v[r] = ((o > v[r]) == (lower == desc)) ? o : v[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < E; r++) {
+          if ((r & j) == 0) {
+            const int i = lane * E + r;
+            const bool desc = (i & s) == 0;
+            const uint32_t p = v[r], q = v[r | j];
+            const bool swap = (q > p) == desc;
+            v[r] = swap ? q : p;
+            v[r | j] = swap ? p : q;
+          }
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
+
+// Sorted order of the c (<= 64*E) keys in buf, all with score part in
+// [obase, omax], into v (position p = lane*E + r, descending).  Fast path: a
+// 32-bit network on compressed keys -- score part minus obase, shifted right
+// just enough to fit 32 - IB bits, then IB bits of the key's position in buf --
+// after which the full keys are gathered by position.  Compressed scores are
+// monotone in the true ones, so the order is exact unless two neighbours share
+// a compressed score; then the full 64-bit keys are sorted instead (fp32 ties,
+// or scores a few ulps apart when the range needs a shift).
+template <int E>
+__device__ __forceinline__ void sort_keys(const uint64_t* buf, int c, int lane, uint32_t obase,
+                                          uint32_t omax, uint64_t (&v)[E]) {
+  constexpr int IB = E <= 2 ? 7 : 8;  // position bits (c <= 2^IB)
+  constexpr uint32_t PM = (1u << IB) - 1u;
+  const int sh = max(0, bitlen32(omax - obase) - (32 - IB));
+  uint32_t w[E];
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int i = lane * E + r;
+    w[r] = 0u;  // padding sorts last: a real key has position bits PM - i >= 1 or score bits
+    if (i < c) {
+      const uint32_t o = (uint32_t)(buf[i] >> 32);
+      w[r] = (((o - obase) >> sh) << IB) | (PM - (uint32_t)i);
+    }
+  }
+  bitonic_desc32<E>(w, lane);
+  bool tie = false;
+#pragma unroll
+  for (int r = 0; r + 1 < E; r++) tie |= lane * E + r + 1 < c && (w[r] >> IB) == (w[r + 1] >> IB);
+  const uint32_t nx = (uint32_t)__shfl_down((int)w[0], 1);  // lane + 1's first
+  tie |= lane < 63 && lane * E + E < c && (w[E - 1] >> IB) == (nx >> IB);
+  if (__ballot(tie) == 0ull) {
+#pragma unroll
+    for (int r = 0; r < E; r++) v[r] = lane * E + r < c ? buf[PM - (w[r] & PM)] : 0ull;
+  } else {
+#pragma unroll
+    for (int r = 0; r < E; r++) {
+      const int i = lane * E + r;
+      v[r] = i < c ? buf[i] : 0ull;
+    }
+    bitonic_desc<E>(v, lane);
+  }
+}
+
+// sort_emit for keys with score part in [obase, omax] (see sort_keys); buf may
+// be overwritten by emit (every key is read before the first write).
+template <typename Emit>
+__device__ __forceinline__ void sort_emit_range(uint64_t* buf, int c, int k, int lane,
+                                                uint32_t obase, uint32_t omax, Emit emit) {
+  auto run = [&](auto tag) {
+    constexpr int E = decltype(tag)::value;
+    uint64_t v[E];
+    sort_keys<E>(buf, c, lane, obase, omax, v);
+#pragma unroll
+    for (int r = 0; r < E; r++) {
+      const int i = lane * E + r;
+      if (i < k) emit(i, v[r]);
+    }
+  };
+  if (c <= 64) run(std::integral_constant<int, 1>{});
+  else if (c <= 128) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 4>{});
 }
 
 // Compact keys >= t into buf (ballot order); returns the count.
@@ -368,16 +468,12 @@ __device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int la
 // Returns false when the frontier could compete (the caller then ranks the
 // full grid).
 template <int E>
-__device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, const uint64_t* L1,
+__device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32_t obase,
+                                              uint32_t omax, const uint64_t* L1,
                                               const uint64_t* L2, int m, int k, int n_sub,
                                               int lane, int32_t* dst_i, float* dst_w) {
   uint64_t v[E];
-#pragma unroll
-  for (int r = 0; r < E; r++) {
-    const int i = lane * E + r;
-    v[r] = i < c ? buf[i] : 0ull;
-  }
-  bitonic_desc<E>(v, lane);
+  sort_keys<E>(buf, c, lane, obase, omax, v);
   // k-th best key: position k-1 = lane (k-1)/E, register (k-1)%E
   uint64_t kv = v[0];
 #pragma unroll
@@ -441,9 +537,10 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
   const int c = compact_ge(key, t, buf, lane);
   wave_lds_sync();
   bool done;
-  if (c <= 64) done = stage2_sorted<1>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
-  else if (c <= 128) done = stage2_sorted<2>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
-  else done = stage2_sorted<4>(buf, c, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  const uint32_t ob = (uint32_t)(t >> 32), om = (uint32_t)(mx >> 32);
+  if (c <= 64) done = stage2_sorted<1>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  else if (c <= 128) done = stage2_sorted<2>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  else done = stage2_sorted<4>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
   if (done) return;
 
   // rare: rank the full m x m grid.  The k-th key of the pruned grid is a
@@ -534,6 +631,7 @@ __global__ void __launch_bounds__(kThreads, 4)
   __shared__ float2 s_stat[kWaves][kCols];    // per wave: sum, sum of squares
   __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
   __shared__ int s_cnt[2][kWaves][kCols];     // per wave: #{keys >= t}, two rounds
+  __shared__ uint32_t s_range[2][kCols];      // per column: score part of t, largest score part
   const ScoreSmem L = score_smem(a.W, a.R);
   const int m = L.m, cm = L.capmax;
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
@@ -660,6 +758,7 @@ __global__ void __launch_bounds__(kThreads, 4)
         it++;
       }
       const int fin = it & 1;
+      if (hw == 0 && kq == 0) s_range[0][tl] = (uint32_t)(t >> 32), s_range[1][tl] = omax;
       // pack this lane's keys >= t behind those of earlier waves and lanes
       int pos = 0;
       for (int w = 0; w < hw; w++) pos += s_cnt[fin][w][tl];
@@ -716,7 +815,8 @@ __global__ void __launch_bounds__(kThreads, 4)
           for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
           c = min(c, cm);
           uint64_t* lst = cand + cc * 2 * cm + half * m;
-          sort_emit(cand + (cc * 2 + half) * cm, c, k, hl, [&](int r, uint64_t kk) { lst[r] = kk; });
+          sort_emit_range(cand + (cc * 2 + half) * cm, c, k, hl, s_range[0][cc], s_range[1][cc],
+                          [&](int r, uint64_t kk) { lst[r] = kk; });
         }
       }
     }
