@@ -8,7 +8,8 @@
 // p = S k and r = S q taken from the old state:
 //   e = beta (v - alpha p),  o = alpha r + e (k . q),  S <- alpha S + e k^T
 // (o = S_t q expanded with S_t = alpha S + e k^T).  The two row reductions
-// over the 16 column tiles of a row run as one reduce-scatter butterfly.
+// over the 16 column tiles of a row run as one reduce-scatter butterfly; all
+// cross-lane moves stay inside 16-lane DPP rows (no LDS round trips).
 // Bound: fp32 VALU (4 d_v d_k FMA per token), not HBM.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,6 +26,12 @@ constexpr int kTC = 16;         // tokens staged per chunk
 constexpr int kChunkF4 = kTC * (3 * kD + 4) / 4;  // float4 per chunk (k, q, v, gates)
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// v of lane n of this lane's row of 16 (DPP row broadcast)
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
 
 }  // namespace
 
@@ -74,7 +81,6 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
   const int rg = tid >> 4;        // row tile: rows 4rg .. 4rg+3
   const int b0 = cg & 1, b1 = (cg >> 1) & 1, b2 = (cg >> 2) & 1, b3 = (cg >> 3) & 1;
   const int lane = tid & 63;
-  const int seg16 = lane & ~15;   // first lane of this row group's 16
 
   float* Sg = a.S + (int64_t)st * kD * kD;
   float s[4][8];
@@ -139,39 +145,38 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
       for (int u = 0; u < 4; u++) {
         const float send = b3 ? val[u] : val[4 + u];
         const float keep = b3 ? val[4 + u] : val[u];
-        h4[u] = keep + __shfl_xor(send, 8);
+        h4[u] = keep + xor_shuffle(send, 8, lane);
       }
       float h2[2];
 #pragma unroll
       for (int u = 0; u < 2; u++) {
         const float send = b2 ? h4[u] : h4[2 + u];
         const float keep = b2 ? h4[2 + u] : h4[u];
-        h2[u] = keep + __shfl_xor(send, 4);
+        h2[u] = keep + xor_shuffle(send, 4, lane);
       }
       float h1;
       {
         const float send = b1 ? h2[0] : h2[1];
         const float keep = b1 ? h2[1] : h2[0];
-        h1 = keep + __shfl_xor(send, 2);
+        h1 = keep + xor_shuffle(send, 2, lane);
       }
-      h1 += __shfl_xor(h1, 1);
-      kq += __shfl_xor(kq, 1);
-      kq += __shfl_xor(kq, 2);
-      kq += __shfl_xor(kq, 4);
-      kq += __shfl_xor(kq, 8);
+      h1 += xor_shuffle(h1, 1, lane);
+      kq += xor_shuffle(kq, 1, lane);
+      kq += xor_shuffle(kq, 2, lane);
+      kq += xor_shuffle(kq, 4, lane);
+      kq += xor_shuffle(kq, 8, lane);
       // lane holds row ri = 2b2+b1 of the tile: p if b3 == 0, r if b3 == 1
       const int ri = 2 * b2 + b1;
       const float vrow = V[tt * kD + 4 * rg + ri];
       const float e_own = beta * (vrow - alpha * h1);    // meaningful where b3 == 0
-      const float e_row = __shfl_xor(e_own, 8);          // e of the row, at b3 == 1
+      const float e_row = xor_shuffle(e_own, 8, lane);   // e of the row, at b3 == 1
       if (b3 == 1 && b0 == 0 && tc0 + tt < a.T) {
         const float o = fmaf(alpha, h1, e_row * kq);
         a.out[((int64_t)st * a.T + tc0 + tt) * kD + 4 * rg + ri] = o;
       }
       // e of the tile's 4 rows (held at lanes b3=0, 2b2+b1 = i)
-      float e[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) e[i] = __shfl(e_own, seg16 + 2 * i);
+      const float e[4] = {row_bcast<0>(e_own), row_bcast<2>(e_own), row_bcast<4>(e_own),
+                          row_bcast<6>(e_own)};
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll

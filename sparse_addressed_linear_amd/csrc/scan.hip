@@ -460,7 +460,7 @@ ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R) {
   // events per token and partition to fill a wave.
   int P = 1;
   while (P < 64 && (int64_t)S * p.CS * (P * 2) <= kTargetWorkgroups &&
-         (W + R) / (P * 2) >= 16 && P * 2 <= N)
+         (W + R) / (P * 2) >= 8 && P * 2 <= N)
     P *= 2;
   p.P = P;
   // registers per lane group: the mean events of a token in one partition
