@@ -14,7 +14,8 @@ extern template hipError_t launch_score_t<4>(const ScoreArgs&, bool, int, hipStr
 extern template hipError_t launch_score_t<8>(const ScoreArgs&, bool, int, hipStream_t);
 
 // Sub-key tables in the order the MFMA A operand takes them: for head h, half
-// c, tile t (sub-keys 16t .. 16t+15) and K step ks (elements 32ks .. 32ks+31),
+// c, tile t (sub-keys 16t .. 16t+15) and K step ks < score_ksteps(dh)
+// (elements 32ks .. 32ks+31),
 // 64 pieces of 8 bf16, piece l = sub-key 16t + l%16, elements
 // 32ks + 8*(l/16) .. +8 (zero past dh).  One thread per 16-byte piece.
 __global__ void __launch_bounds__(256) sdm_pack_subkeys_kernel(const uint16_t* __restrict__ C,
@@ -39,8 +40,7 @@ __global__ void __launch_bounds__(256) sdm_pack_subkeys_kernel(const uint16_t* _
 
 size_t score_topk_workspace_bytes(int H, int n_sub, int d_k, bool bf16) {
   if (!bf16) return 0;
-  const int ksteps = (d_k / 2 + 31) / 32;
-  return (size_t)H * 2 * (n_sub / 16) * ksteps * 1024;
+  return (size_t)H * 2 * (n_sub / 16) * score_ksteps(d_k / 2) * 1024;
 }
 
 size_t score_topk_lds_bytes(int n_sub, int W, int R) {
@@ -53,7 +53,7 @@ hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream) 
   if (bf16 && a.packed == nullptr) return hipErrorInvalidValue;  // the packed fragments' home
   if (bf16) {
     const int dh = a.d_k / 2;
-    const int ksteps = (dh + 31) / 32;
+    const int ksteps = score_ksteps(dh);
     const int64_t pieces = (int64_t)a.H * 2 * (a.n_sub / 16) * ksteps * 64;
     hipLaunchKernelGGL(sdm_pack_subkeys_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256),
                        0, stream, static_cast<const uint16_t*>(a.subkeys),

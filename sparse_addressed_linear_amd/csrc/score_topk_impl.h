@@ -55,16 +55,24 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kCapMax = 256;    // largest candidate set sorted at once
 constexpr int kGridMax = 704;   // largest pruned grid held in registers (11 per lane)
 
+// K steps of 32 per sub-key row in the packed fragments: the MFMA template
+// count for dh (1, 2, 4 or 8; rows are zero-padded to it)
+__host__ __device__ inline int score_ksteps(int dh) {
+  return dh <= 32 ? 1 : dh <= 64 ? 2 : dh <= 128 ? 4 : 8;
+}
+
 // candidates kept for a top-k: between k and this many
 __host__ __device__ inline int cap_for(int k) {
   const int c = 2 * k > 64 ? 2 * k : 64;
   return c < kCapMax ? c : kCapMax;
 }
 
+// order-preserving code of a finite float: sign bit flipped for s >= 0, all
+// bits flipped for s < 0; adding +0 first turns -0 into +0, so both zeros
+// rank equal
 __device__ __forceinline__ uint32_t ord32(float s) {
-  uint32_t u = __float_as_uint(s);
-  if ((u << 1) == 0u) u = 0u;  // -0 ranks equal to +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float unord32(uint32_t o) {
@@ -77,6 +85,13 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
 }
 __device__ __forceinline__ float key_score(uint64_t k) { return unord32((uint32_t)(k >> 32)); }
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+
+// stage-1 list entry: score bits in the low word, sub-key id in the high word
+__device__ __forceinline__ uint64_t list_entry(uint64_t key) {
+  return ((uint64_t)key_id(key) << 32) | __float_as_uint(key_score(key));
+}
+__device__ __forceinline__ float entry_score(uint64_t e) { return __uint_as_float((uint32_t)e); }
+__device__ __forceinline__ uint32_t entry_id(uint64_t e) { return (uint32_t)(e >> 32); }
 
 // sum over e ascending of x[e]*c[e], each product and sum rounded in fp32
 __device__ __forceinline__ float dot_seq(const float* x, const float* c, int n) {
@@ -93,6 +108,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   const int lane = __lane_id();
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += xor_shuffle(x, o, lane);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max32(uint32_t x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, xor_shuffle(x, o, lane));
   return x;
 }
 __device__ __forceinline__ uint64_t wave_max64(uint64_t x) {
@@ -452,7 +473,7 @@ __device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int la
     e[r] = p < k ? __expf(key_score(v[r]) - top) : 0.f;
     z += e[r];
   }
-  const float iz = 1.0f / wave_sum(z);
+  const float iz = __builtin_amdgcn_rcpf(wave_sum(z));
 #pragma unroll
   for (int r = 0; r < E; r++) {
     const int p = lane * E + r;
@@ -470,8 +491,8 @@ __device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int la
 template <int E>
 __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32_t obase,
                                               uint32_t omax, const uint64_t* L1,
-                                              const uint64_t* L2, int m, int k, int n_sub,
-                                              int lane, int32_t* dst_i, float* dst_w) {
+                                              const uint64_t* L2, const int32_t* rowoff, int m,
+                                              int k, int lane, int32_t* dst_i, float* dst_w) {
   uint64_t v[E];
   sort_keys<E>(buf, c, lane, obase, omax, v);
   // k-th best key: position k-1 = lane (k-1)/E, register (k-1)%E
@@ -487,9 +508,9 @@ __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32
   float fr = -INFINITY;
   bool any = false;
   for (int ra = lane; ra < m; ra += 64) {
-    const int rb = min(m, k / (ra + 1));
+    const int rb = rowoff[ra + 1] - rowoff[ra];  // row ra of the grid: ranks 0 .. rb-1
     if (rb < m) {
-      const float s = key_score(L1[ra]) + key_score(L2[rb]);
+      const float s = entry_score(L1[ra]) + entry_score(L2[rb]);
       fr = any ? fmaxf(fr, s) : s;
       any = true;
     }
@@ -500,15 +521,18 @@ __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32
   return true;
 }
 
-// Stage 2 for one column whose stage-1 lists (rank-ordered keys) are L1, L2:
-// the k best slots over the pruned grid, written in rank order with their
-// softmax weights.  buf holds cap_for(k) keys of scratch.
+// Stage 2 for one column whose stage-1 lists (rank order, list_entry form)
+// are L1, L2: the k best slots over the pruned grid (row offsets rowoff),
+// written in rank order with their softmax weights.  buf holds cap_for(k)
+// keys of scratch.
 template <int NPL2>
 __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, int m, int k,
-                                       int n_sub, const uint32_t* grid, int G, float z,
-                                       uint64_t* buf, int lane, int32_t* dst_i, float* dst_w) {
+                                       int n_sub, const uint32_t* grid, const int32_t* rowoff,
+                                       int G, float z, uint64_t* buf, int lane, int32_t* dst_i,
+                                       float* dst_w) {
   uint64_t key[NPL2];
   float sum = 0.f, sq = 0.f;
+  uint32_t mo = 0u;  // largest score code
 #pragma unroll
   for (int j = 0; j < NPL2; j++) {
     const int c = j * 64 + lane;
@@ -516,31 +540,30 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
     if (c < G) {
       const uint32_t ab = grid[c];
       const uint64_t a1 = L1[ab >> 16], a2 = L2[ab & 0xffff];
-      const float s = key_score(a1) + key_score(a2);
-      key[j] = make_key(s, key_id(a1) * (uint32_t)n_sub + key_id(a2));
+      const float s = entry_score(a1) + entry_score(a2);
+      const uint32_t o = ord32(s);
+      key[j] = ((uint64_t)o << 32) | (0xffffffffu - (entry_id(a1) * (uint32_t)n_sub + entry_id(a2)));
+      mo = max(mo, o);
       sum += s;
       sq += s * s;
     }
   }
   const int cap = cap_for(k);
-  uint64_t mx = 0;
-#pragma unroll
-  for (int j = 0; j < NPL2; j++) mx = key[j] > mx ? key[j] : mx;
-  mx = wave_max64(mx);
+  mo = wave_max32(mo);
   // first threshold from the mean and spread of the G sums
   sum = wave_sum(sum);
   sq = wave_sum(sq);
   const float mean = sum / G;
   const float sd = sqrtf(fmaxf(sq / G - mean * mean, 0.f));
   const uint64_t guess = (uint64_t)ord32(mean + z * sd) << 32;
-  const uint64_t t = find_threshold(key, k, cap, guess, 0ull, mx + 1ull);
+  const uint64_t t = find_threshold(key, k, cap, guess, 0ull, ((uint64_t)mo + 1ull) << 32);
   const int c = compact_ge(key, t, buf, lane);
   wave_lds_sync();
   bool done;
-  const uint32_t ob = (uint32_t)(t >> 32), om = (uint32_t)(mx >> 32);
-  if (c <= 64) done = stage2_sorted<1>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
-  else if (c <= 128) done = stage2_sorted<2>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
-  else done = stage2_sorted<4>(buf, c, ob, om, L1, L2, m, k, n_sub, lane, dst_i, dst_w);
+  const uint32_t ob = (uint32_t)(t >> 32);
+  if (c <= 64) done = stage2_sorted<1>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
+  else if (c <= 128) done = stage2_sorted<2>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
+  else done = stage2_sorted<4>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
   if (done) return;
 
   // rare: rank the full m x m grid.  The k-th key of the pruned grid is a
@@ -548,7 +571,7 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
   wave_lds_sync();
   auto full_key = [&](int q) {
     const uint64_t a1 = L1[q / m], a2 = L2[q % m];
-    return make_key(key_score(a1) + key_score(a2), key_id(a1) * (uint32_t)n_sub + key_id(a2));
+    return make_key(entry_score(a1) + entry_score(a2), entry_id(a1) * (uint32_t)n_sub + entry_id(a2));
   };
   auto cnt = [&](uint64_t tt) {
     int n = 0;
@@ -586,7 +609,7 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
   const float top = key_score(buf[0]);
   float zs = 0.f;
   for (int r = lane; r < k; r += 64) zs += __expf(key_score(buf[r]) - top);
-  const float iz = 1.0f / wave_sum(zs);
+  const float iz = __builtin_amdgcn_rcpf(wave_sum(zs));
   for (int r = lane; r < k; r += 64) {
     const uint64_t kk = buf[r];
     dst_i[r] = (int32_t)key_id(kk);
@@ -604,10 +627,13 @@ __device__ __forceinline__ void grid_rowoff(int k, int32_t* rowoff, int lane) {
     const int y0 = __shfl_up(s0, o), y1 = __shfl_up(s1, o);
     if (lane >= o) s0 += y0, s1 += y1;
   }
+  // both totals are read with every lane active (a lane shuffle from a lane
+  // that is switched off does not return that lane's value)
   const int tot0 = __shfl(s0, 63);
+  const int tot1 = __shfl(s1, 63);
   if (lane < k) rowoff[lane] = s0 - len0;
   if (lane + 64 < k) rowoff[lane + 64] = tot0 + s1 - len1;
-  if (lane == 0) rowoff[k] = tot0 + __shfl(s1, 63);
+  if (lane == 0) rowoff[k] = tot0 + tot1;
 }
 
 __device__ __forceinline__ void grid_fill(int k, const int32_t* rowoff, uint32_t* grid, int wave,
@@ -678,7 +704,7 @@ __global__ void __launch_bounds__(kThreads, 4)
         const uint16_t* xcol = static_cast<const uint16_t*>(is_q ? a.qp : a.kp) +
                                ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
         const int n_tiles = n_sub / 16;
-        const int ksteps = (dh + 31) / 32;
+        const int ksteps = score_ksteps(dh);
         const unsigned char* Pb = static_cast<const unsigned char*>(a.packed) +
                                   ((int64_t)h * 2 + half) * n_tiles * ksteps * 1024;
         if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
@@ -816,7 +842,7 @@ __global__ void __launch_bounds__(kThreads, 4)
           c = min(c, cm);
           uint64_t* lst = cand + cc * 2 * cm + half * m;
           sort_emit_range(cand + (cc * 2 + half) * cm, c, k, hl, s_range[0][cc], s_range[1][cc],
-                          [&](int r, uint64_t kk) { lst[r] = kk; });
+                          [&](int r, uint64_t kk) { lst[r] = list_entry(kk); });
         }
       }
     }
@@ -831,7 +857,8 @@ __global__ void __launch_bounds__(kThreads, 4)
         const bool own_grid = q && L.gR;
         uint64_t* blk = cand + cc * 2 * cm;
         stage2<NPL2>(blk, blk + m, k, k, a.n_sub, own_grid ? grid + L.gW : grid,
-                     own_grid ? L.gR : L.gW, q ? z.r2 : z.w2, blk + 2 * m, lane,
+                     own_grid ? rowoff + (m + 1) : rowoff, own_grid ? L.gR : L.gW,
+                     q ? z.r2 : z.w2, blk + 2 * m, lane,
                      (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,
                      (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
       }

@@ -22,16 +22,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 // after unrolling.  Cross-lane moves without the LDS crossbar: DPP quad
 // permutes (1, 2), row shifts (4), row rotate (8), the swizzle unit (16) and
 // the gfx950 32-lane swap (32).
+// (mov_dpp leaves lanes without a source undefined: the permutes and the
+// rotate have none, and of the two shifts only lanes that have one are kept)
 __device__ __forceinline__ uint32_t xor_shuffle(uint32_t v, int m, int lane) {
   switch (m) {
-    case 1: return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    case 2: return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    case 1: return __builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    case 2: return __builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
     case 4: {
-      const uint32_t up = __builtin_amdgcn_update_dpp(0u, v, 0x104, 0xF, 0xF, false);  // row_shl:4
-      const uint32_t dn = __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+      const uint32_t up = __builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);  // row_shl:4
+      const uint32_t dn = __builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
       return (lane & 4) ? dn : up;
     }
-    case 8: return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 8: return __builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
     case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);    // xor 16 in 32
     default: {
       const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);

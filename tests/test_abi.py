@@ -112,7 +112,7 @@ def test_scan_rejects(L):
     assert scan(L, dims(), dt=5) == 3
     assert scan(L, dims(d_v=20)) == 4
     assert scan(L, dims(n_sub=64, W=300)) == 4
-    assert scan(L, dims(), ptr=ctypes.c_void_p(4104)) == 5
+    assert scan(L, dims(), ptr=ctypes.c_void_p(4104), ws=1 << 30) == 5
 
 
 def test_scan_workspace_contract(L):

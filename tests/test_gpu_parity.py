@@ -86,7 +86,9 @@ def test_score_topk_integer_ties(dev):
     say("case: integer ties")
     g = torch.Generator().manual_seed(7)
     for (B, H, T, d_k, n_sub, W, R) in ((1, 2, 40, 32, 64, 16, 12), (2, 1, 33, 64, 32, 32, 5),
-                                        (1, 1, 17, 32, 128, 128, 128)):
+                                        (1, 1, 17, 32, 128, 128, 128),
+                                        # sub-key halves of 80 and 96: K padded to 128
+                                        (2, 1, 19, 160, 32, 32, 20), (1, 2, 29, 192, 128, 128, 97)):
         q = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         k = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         C = torch.randint(-1, 2, (H, 2, n_sub, d_k // 2), generator=g).float()
@@ -136,7 +138,13 @@ def test_score_topk_full_size_sampled(dev, name, per_stream):
     say(f"case: {name} addressing, full size, sampled", wl)
     x = synth.make_inputs(wl, device=dev, with_m0=False)
     g = sdm().score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R)
+    g2 = sdm().score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R)
     torch.cuda.synchronize()
+    # a second call gives the same bits, and every slot is a row of the table
+    for a, b2 in zip(g, g2):
+        assert torch.equal(a, b2)
+    for ix in (g[0], g[2]):
+        assert int(ix.min()) >= 0 and int(ix.max()) < wl.N
     rng = np.random.default_rng(wl.seed)
     tot = [0, 0, 0]
     for b in range(wl.B):
