@@ -105,12 +105,134 @@ def cpu_baseline_gdn(wl, x, n_streams):
                       f"({tok} stream-tokens), single-threaded fp32 C"}
 
 
+def cpu_baseline_decode(wl, x, m0_cpu, n_streams):
+    """Oracle (single thread) decoding the same tokens of the first n_streams
+    streams: addressing + scan of every step's token."""
+    import oracle
+    import synth
+    tok, t_total = 0, 0.0
+    for s in range(n_streams):
+        b, h = divmod(s, wl.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        M = synth.to_numpy(m0_cpu[s])[None, None].copy()
+        hq, hk, hv, ha, hb = (synth.to_numpy(x[n][sl]) for n in ("q", "k", "v", "alpha", "beta"))
+        hc = synth.to_numpy(x["subkeys"][h:h + 1])
+        t0 = time.perf_counter()
+        for t in range(wl.T):
+            ts = slice(t, t + 1)
+            r = oracle.score_topk(hq[:, :, ts], hk[:, :, ts], hc, wl.W, wl.R)
+            oracle.scan(M, r["widx"], r["wwt"], r["ridx"], r["rwt"], hv[:, :, ts], ha[:, :, ts],
+                        hb[:, :, ts])
+        t_total += time.perf_counter() - t0
+        tok += wl.T
+    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_streams} of {wl.streams} streams x {wl.T} decoding steps "
+                      f"({tok} stream-tokens), addressing + scan per step, single-threaded fp32 C"}
+
+
+def bench_decode(args, wl, dev):
+    """Decoding: each step scores and scans ONE new token of every stream
+    (head-major layouts, sub-keys packed once).  The timed K steps are captured
+    in one HIP graph, each step reading its own token's inputs, and the graph
+    is replayed once: the time is the device time of K back-to-back steps,
+    without host launch overhead.  The eager per-step wall time (host launch
+    overhead included) is reported beside it."""
+    import torch
+
+    import sparse_addressed_linear_amd as sdm
+    import synth
+    K, Wm = args.steps, args.warmup
+    wl = wl.with_(T=max(wl.T, 2 * Wm + 2 * K))
+    print(f"[bench] workload {wl.name}: generating inputs on the device", file=sys.stderr,
+          flush=True)
+    x = synth.make_inputs(wl, device=dev, with_m0=False)
+    xd = synth.decode_layout(x)
+    M = synth.make_m0(wl, dev, head_major=True)
+    n_cpu = min(args.cpu_streams if args.cpu_streams is not None else 8, wl.streams)
+    m0_cpu = [M[s % wl.H, s // wl.H].cpu() for s in range(n_cpu)]
+    packed = sdm.pack_subkeys(x["subkeys"])
+    bufs = {}
+    H, B = wl.H, wl.B
+    stream = torch.cuda.current_stream()
+
+    def step(t, ev=None):
+        if ev:
+            ev[0].record(stream)
+        idx = sdm.score_topk(xd["q"][t].view(1, H, B, wl.d_k), xd["k"][t].view(1, H, B, wl.d_k),
+                             xd["subkeys"], wl.W, wl.R, out=bufs.get("idx"), packed=packed)
+        bufs["idx"] = idx
+        if ev:
+            ev[1].record(stream)
+        v = [t_.view(H, B, 1, -1) for t_ in idx]
+        bufs["out"] = sdm.scan(M, *v, xd["v"][t].view(H, B, 1, wl.d_v),
+                               xd["alpha"][t].view(H, B, 1), xd["beta"][t].view(H, B, 1),
+                               out=bufs.get("out"), workspace=bufs.get("ws"))
+        if ev:
+            ev[2].record(stream)
+
+    need = sdm.scan_workspace_size(H, B, 1, wl.N, wl.d_v, wl.W, wl.R)
+    bufs["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    t = 0
+    for _ in range(Wm):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    # eager: per-step events and wall time
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(t, evs[i])
+        t += 1
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / K
+    ms_score = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    ms_scan = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    # graph of K steps (tokens t .. t+K-1), replayed once
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(K):
+                step(t + i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {K} decoding steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    value = wl.streams / (ms_step * 1e-3)
+    sbytes = wl.streams * scan_bytes_per_token(wl)
+    achieved = sbytes / (ms_scan * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": "sdm_scan (one token per stream)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
+    cpu = None
+    if n_cpu:
+        print(f"[bench] CPU baseline: oracle on {n_cpu} streams", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_decode(wl.with_(T=K), x, m0_cpu, n_cpu)
+    cfg = {"workload": wl.name, "B": wl.B, "H": wl.H, "tokens_per_step": 1, "d_k": wl.d_k,
+           "d_v": wl.d_v, "n_sub": wl.n_sub, "N": wl.N, "W": wl.W, "R": wl.R, "inputs": "bf16",
+           "table": "fp32", "table_GB": round(wl.table_bytes() / 1e9, 2),
+           "timing": f"{K} steps in one HIP graph, replayed once"}
+    line = {"metric": "SDM decoding: stream-tokens/sec (one token per stream per step) at N=2^20",
+            "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+            "warmup": Wm, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "kernels": {"score_topk_ms": round(ms_score, 5), "scan_ms": round(ms_scan, 5),
+                        "eager_wall_ms_per_step": round(eager_ms, 5)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="large", choices=["tiny", "mid", "large", "long", "gdn"])
+    ap.add_argument("--config", default="large",
+                    choices=["tiny", "mid", "large", "long", "gdn", "decode"])
     ap.add_argument("--cpu-streams", type=int, default=None,
                     help="streams in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
@@ -144,6 +266,9 @@ def main():
     sdm.lib()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.config]
+    if wl.name == "decode":
+        bench_decode(args, wl, dev)
+        return
 
     print(f"[bench] workload {wl.name}: generating inputs on the device", file=sys.stderr,
           flush=True)

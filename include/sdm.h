@@ -102,6 +102,30 @@ int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, con
 size_t sdm_score_topk_workspace_size(const sdm_dims* dims, sdm_dtype in_dtype);
 
 /*
+ * sdm_pack_subkeys / sdm_score_topk_packed -- the same addressing split in two,
+ * for callers that score many short calls against fixed sub-key tables (one
+ * token per stream per call when decoding; Spanish page "Resultados
+ * Experimentales", ablations, efficiency at inference).
+ *
+ * sdm_pack_subkeys writes the matrix-core copy of `subkeys` into `workspace`
+ * (the copy sdm_score_topk makes on every call); only dims->H, d_k and n_sub
+ * are used.  With fp32 inputs nothing needs packing and it returns SDM_OK
+ * without touching the workspace.  sdm_score_topk_packed then scores as
+ * sdm_score_topk does, reading the packed tables from `workspace` (read only;
+ * the caller keeps it unchanged and owns it) instead of repacking them.  The
+ * workspace must have been filled by sdm_pack_subkeys for the same H, d_k,
+ * n_sub and sub-key values, on this stream or one ordered before it; results
+ * are otherwise undefined.  `subkeys` is still passed (fp32 inputs read it).
+ * Arguments, limits and errors are those of sdm_score_topk.
+ */
+int sdm_pack_subkeys(const sdm_dims* dims, sdm_dtype in_dtype, const void* subkeys,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int sdm_score_topk_packed(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp,
+                          const void* kp, const void* subkeys, int32_t* widx, float* wwt,
+                          int32_t* ridx, float* rwt, const void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * sdm_scan -- sparse gated-delta write and sparse read over the memory table
  * (Spanish page "Mecanismo Central" items 1, 3 and 4; French page
  * "Mecanisme Central").

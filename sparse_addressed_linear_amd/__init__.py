@@ -23,8 +23,9 @@ SDM_F32, SDM_BF16 = 0, 1
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE",
           4: "SDM_ERR_UNSUPPORTED", 5: "SDM_ERR_ALIGN", 6: "SDM_ERR_HIP",
           7: "SDM_ERR_WORKSPACE"}
-EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_scan",
-           "sdm_scan_workspace_size", "sdm_gdn_scan", "sdm_status_str", "sdm_version")
+EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
+           "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
+           "sdm_status_str", "sdm_version")
 
 
 class SdmError(RuntimeError):
@@ -53,6 +54,10 @@ def lib():
         PD = ctypes.POINTER(Dims)
         L.sdm_score_topk.argtypes = [PD, I32, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_score_topk.restype = ctypes.c_int
+        L.sdm_pack_subkeys.argtypes = [PD, I32, P, P, SZ, P]
+        L.sdm_pack_subkeys.restype = ctypes.c_int
+        L.sdm_score_topk_packed.argtypes = [PD, I32, P, P, P, P, P, P, P, P, SZ, P]
+        L.sdm_score_topk_packed.restype = ctypes.c_int
         L.sdm_score_topk_workspace_size.argtypes = [PD, I32]
         L.sdm_score_topk_workspace_size.restype = SZ
         L.sdm_scan.argtypes = [PD, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -103,11 +108,33 @@ def _check(fn, rc):
         raise SdmError(fn, rc)
 
 
-def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None):
+def pack_subkeys(subkeys, workspace=None, stream=None):
+    """Matrix-core copy of the sub-key tables [H,2,n_sub,d_k/2] for
+    ``score_topk(..., packed=...)``: a uint8 device tensor, or None for fp32
+    tables (nothing to pack)."""
+    H, two, n_sub, dh = subkeys.shape
+    if two != 2:
+        raise ValueError("subkeys must be [H,2,n_sub,d_k/2]")
+    dt = _dtype_code(subkeys)
+    d = Dims(1, H, 1, 2 * dh, n_sub, 1, 1, 1)
+    need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
+    if need == 0:
+        return None
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=subkeys.device)
+    rc = lib().sdm_pack_subkeys(ctypes.byref(d), dt, _dev(subkeys, "subkeys"),
+                                _dev(workspace, "workspace"), ctypes.c_size_t(need),
+                                _stream(stream))
+    _check("sdm_pack_subkeys", rc)
+    return workspace
+
+
+def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None, packed=None):
     """Product-key addressing.  qp, kp: [B,H,T,d_k]; subkeys: [H,2,n_sub,d_k/2]
     (all fp32 or all bf16).  Returns (widx, wwt, ridx, rwt): [B,H,T,W] int32,
     fp32 and [B,H,T,R] int32, fp32, in rank order.  ``workspace`` (uint8 device
-    tensor) is allocated here when not given or too small."""
+    tensor) is allocated here when not given or too small.  ``packed``, from
+    ``pack_subkeys(subkeys)``, skips repacking the sub-key tables."""
     B, H, T, d_k = qp.shape
     if kp.shape != qp.shape or subkeys.dim() != 4 or subkeys.shape[0] != H or \
             subkeys.shape[1] != 2 or subkeys.shape[3] * 2 != d_k:
@@ -123,15 +150,20 @@ def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None):
     widx, wwt, ridx, rwt = out
     d = Dims(B, H, T, d_k, n_sub, 1, W, R)
     need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+    fn = "sdm_score_topk"
+    if packed is not None and need:
+        if packed.numel() * packed.element_size() < need:
+            raise ValueError("packed sub-keys are smaller than these sizes need")
+        workspace, fn = packed, "sdm_score_topk_packed"
+    elif need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
-    rc = lib().sdm_score_topk(ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"),
-                              _dev(subkeys, "subkeys"), _dev(widx, "widx", torch.int32),
-                              _dev(wwt, "wwt", torch.float32), _dev(ridx, "ridx", torch.int32),
-                              _dev(rwt, "rwt", torch.float32), wsp, ctypes.c_size_t(need),
-                              _stream(stream))
-    _check("sdm_score_topk", rc)
+    rc = getattr(lib(), fn)(ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"),
+                            _dev(subkeys, "subkeys"), _dev(widx, "widx", torch.int32),
+                            _dev(wwt, "wwt", torch.float32), _dev(ridx, "ridx", torch.int32),
+                            _dev(rwt, "rwt", torch.float32), wsp, ctypes.c_size_t(need),
+                            _stream(stream))
+    _check(fn, rc)
     return widx, wwt, ridx, rwt
 
 
@@ -175,6 +207,44 @@ def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stre
                         wsp, ctypes.c_size_t(need), _stream(stream))
     _check("sdm_scan", rc)
     return out
+
+
+def decode_step(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, bufs=None,
+                stream=None):
+    """One decoding step: one new token for every stream, addressing then scan.
+
+    Head-major layouts, so that the tokens of one head (which share its
+    sub-key tables) are scored together:  M [H,B,N,d_v] fp32 (updated in
+    place), qp, kp [H,B,d_k], v [H,B,d_v], alpha, beta [H,B], subkeys
+    [H,2,n_sub,d_k/2].  Stream (b,h) of the sequence layout is row (h,b) here.
+    ``packed`` is ``pack_subkeys(subkeys)``; ``bufs`` (a dict, filled on
+    first use) keeps the slot lists, output and scan workspace between steps.
+    Returns out [H,B,d_v] fp32."""
+    H, B, N, d_v = M.shape
+    d_k = qp.shape[-1]
+    if qp.shape != (H, B, d_k) or kp.shape != qp.shape or v.shape != (H, B, d_v) or \
+            alpha.shape != (H, B) or beta.shape != (H, B):
+        raise ValueError("shape mismatch in decode_step arguments")
+    bufs = {} if bufs is None else bufs
+    dev = M.device
+    if "idx" not in bufs:
+        bufs["idx"] = (torch.empty((1, H, B, W), dtype=torch.int32, device=dev),
+                       torch.empty((1, H, B, W), dtype=torch.float32, device=dev),
+                       torch.empty((1, H, B, R), dtype=torch.int32, device=dev),
+                       torch.empty((1, H, B, R), dtype=torch.float32, device=dev))
+        bufs["out"] = torch.empty((H, B, 1, d_v), dtype=torch.float32, device=dev)
+        need = scan_workspace_size(H, B, 1, N, d_v, W, R)
+        bufs["scan_ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        need = 0 if packed is not None else score_topk_workspace_size(
+            1, H, B, d_k, subkeys.shape[2], W, R, bf16=subkeys.dtype == torch.bfloat16)
+        bufs["score_ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    widx, wwt, ridx, rwt = score_topk(qp.view(1, H, B, d_k), kp.view(1, H, B, d_k), subkeys, W, R,
+                                      out=bufs["idx"], workspace=bufs.get("score_ws"),
+                                      stream=stream, packed=packed)
+    out = scan(M, widx.view(H, B, 1, W), wwt.view(H, B, 1, W), ridx.view(H, B, 1, R),
+               rwt.view(H, B, 1, R), v.view(H, B, 1, d_v), alpha.view(H, B, 1),
+               beta.view(H, B, 1), out=bufs["out"], workspace=bufs.get("scan_ws"), stream=stream)
+    return out.view(H, B, d_v)
 
 
 def gdn_scan(S, k, q, v, alpha, beta, out=None, stream=None):

@@ -48,17 +48,22 @@ size_t score_topk_lds_bytes(int n_sub, int W, int R) {
   return score_smem(W, R).total;
 }
 
-hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream) {
+hipError_t launch_pack_subkeys(const ScoreArgs& a, hipStream_t stream) {
+  if (a.packed == nullptr) return hipErrorInvalidValue;  // the packed fragments' home
+  const int dh = a.d_k / 2;
+  const int ksteps = score_ksteps(dh);
+  const int64_t pieces = (int64_t)a.H * 2 * (a.n_sub / 16) * ksteps * 64;
+  hipLaunchKernelGGL(sdm_pack_subkeys_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(a.subkeys),
+                     static_cast<uint4*>(a.packed), pieces, a.n_sub, dh, ksteps);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, bool pack, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (bf16 && a.packed == nullptr) return hipErrorInvalidValue;  // the packed fragments' home
-  if (bf16) {
-    const int dh = a.d_k / 2;
-    const int ksteps = score_ksteps(dh);
-    const int64_t pieces = (int64_t)a.H * 2 * (a.n_sub / 16) * ksteps * 64;
-    hipLaunchKernelGGL(sdm_pack_subkeys_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(a.subkeys),
-                       static_cast<uint4*>(a.packed), pieces, a.n_sub, dh, ksteps);
-    const hipError_t e = hipGetLastError();
+  if (bf16 && pack) {
+    const hipError_t e = launch_pack_subkeys(a, stream);
     if (e != hipSuccess) return e;
   }
   const int tiles = (a.n_sub + 15) / 16;

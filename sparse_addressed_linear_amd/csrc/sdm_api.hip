@@ -39,9 +39,10 @@ size_t sdm_score_topk_workspace_size(const sdm_dims* d, sdm_dtype in_dtype) {
   return sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
 }
 
-int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
-                   const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+// checks shared by the addressing entry points (everything but the workspace)
+static int check_score(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                       const void* subkeys, const void* widx, const void* wwt,
+                       const void* ridx, const void* rwt) {
   if (!d || !subkeys) return SDM_ERR_NULL;
   int rc = check_dims(d);
   if (rc) return rc;
@@ -56,13 +57,21 @@ int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const 
   if (!aligned16(qp) || !aligned16(kp) || !aligned16(subkeys) || !aligned16(widx) ||
       !aligned16(wwt) || !aligned16(ridx) || !aligned16(rwt))
     return SDM_ERR_ALIGN;
+  return SDM_OK;
+}
+
+static int run_score(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                     const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
+                     const void* workspace, size_t workspace_bytes, bool pack, void* stream) {
+  int rc = check_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt);
+  if (rc) return rc;
   if (d->T == 0) return SDM_OK;
   const size_t need =
       sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SDM_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return SDM_ERR_ALIGN;
   sdm::ScoreArgs a{};
-  a.packed = workspace;
+  a.packed = const_cast<void*>(workspace);  // written only when pack is set
   a.qp = qp;
   a.kp = kp;
   a.subkeys = subkeys;
@@ -77,8 +86,47 @@ int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const 
   a.n_sub = d->n_sub;
   a.W = d->W;
   a.R = d->R;
-  hipError_t e = sdm::launch_score_topk(a, in_dtype == SDM_BF16, (hipStream_t)stream);
+  hipError_t e = sdm::launch_score_topk(a, in_dtype == SDM_BF16, pack, (hipStream_t)stream);
   return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+int sdm_score_topk(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                   const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return run_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt, workspace,
+                   workspace_bytes, true, stream);
+}
+
+int sdm_pack_subkeys(const sdm_dims* d, sdm_dtype in_dtype, const void* subkeys, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!d || !subkeys) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
+  const int dh = d->d_k / 2;
+  if (d->n_sub > 1024 || d->n_sub % 16 != 0 || dh % 16 != 0 || dh > 256) return SDM_ERR_UNSUPPORTED;
+  if (!aligned16(subkeys)) return SDM_ERR_ALIGN;
+  const size_t need =
+      sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
+  if (need == 0) return SDM_OK;  // fp32 sub-keys are read as they are
+  if (!workspace || workspace_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SDM_ERR_ALIGN;
+  sdm::ScoreArgs a{};
+  a.packed = workspace;
+  a.subkeys = subkeys;
+  a.H = d->H;
+  a.d_k = d->d_k;
+  a.n_sub = d->n_sub;
+  hipError_t e = sdm::launch_pack_subkeys(a, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+int sdm_score_topk_packed(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                          const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx,
+                          float* rwt, const void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return run_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt, workspace,
+                   workspace_bytes, false, stream);
 }
 
 size_t sdm_scan_workspace_size(const sdm_dims* d) {

@@ -109,7 +109,9 @@ struct ScoreArgs {
   int32_t S, H, T, d_k, n_sub, W, R;
 };
 
-hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, hipStream_t stream);
+// pack: repack the bf16 sub-keys into `packed` first (else it already holds them)
+hipError_t launch_score_topk(const ScoreArgs& a, bool bf16, bool pack, hipStream_t stream);
+hipError_t launch_pack_subkeys(const ScoreArgs& a, hipStream_t stream);
 size_t score_topk_workspace_bytes(int H, int n_sub, int d_k, bool bf16);
 
 struct GdnArgs {

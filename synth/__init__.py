@@ -21,6 +21,10 @@ configurations; N(mu, var) names a variance):
           head plus N(0, 0.1^2) noise (queries pick prototypes independently).
 * gdn   : dense gated-delta baseline, B=16 H=16 T=8192 d_k=d_v=128, fp32;
           k, q = g/|g| with g ~ N(0, I); v ~ N(0,1); gates as tiny; S0 = 0.
+* decode: serving batch of B=32 sequences x H=8 heads at large's per-stream
+          shape and distributions, T=64 decoding steps of one token each;
+          `decode_layout` gives the step-major, head-major tensors and
+          `make_m0(..., head_major=True)` the table as [H,B,N,d_v].
 """
 from dataclasses import dataclass, replace
 from typing import Optional
@@ -86,6 +90,8 @@ WORKLOADS = {
                      R=128, bf16=True, m0_std=0.1, keys="proto"),
     "gdn": Workload("gdn", 4, B=16, H=16, T=8192, d_k=128, n_sub=0, d_v=128, W=0, R=0,
                     bf16=False, m0_std=0.0, dense=True),
+    "decode": Workload("decode", 5, B=32, H=8, T=64, d_k=128, n_sub=1024, d_v=64, W=64, R=64,
+                       bf16=True, m0_std=0.1, head_scale=(0.5, 2.0)),
 }
 
 
@@ -150,12 +156,24 @@ def make_inputs(wl: Workload, device="cpu", with_m0: bool = True) -> dict:
     return out
 
 
-def make_m0(wl: Workload, device="cpu") -> torch.Tensor:
-    """Initial memory table M0 [B,H,N,d_v] fp32."""
-    shape = (wl.B, wl.H, wl.N, wl.d_v)
+def make_m0(wl: Workload, device="cpu", head_major: bool = False) -> torch.Tensor:
+    """Initial memory table M0 [B,H,N,d_v] fp32 ([H,B,N,d_v] when head_major)."""
+    shape = (wl.H, wl.B, wl.N, wl.d_v) if head_major else (wl.B, wl.H, wl.N, wl.d_v)
     if wl.m0_std == 0.0:
         return torch.zeros(shape, device=device, dtype=torch.float32)
     return _randn(wl, "m0", shape, device, std=wl.m0_std)
+
+
+def decode_layout(x: dict) -> dict:
+    """Per-token inputs of make_inputs rearranged for decoding one token per
+    stream per step: q, k [T,H,B,d_k], v [T,H,B,d_v], alpha, beta [T,H,B]
+    (step t, head h, sequence b); subkeys unchanged."""
+    out = {"subkeys": x["subkeys"]}
+    for name in ("q", "k", "v"):
+        out[name] = x[name].permute(2, 1, 0, 3).contiguous()
+    for name in ("alpha", "beta"):
+        out[name] = x[name].permute(2, 1, 0).contiguous()
+    return out
 
 
 def to_numpy(t: torch.Tensor):

@@ -26,8 +26,9 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
-        ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_scan",
-         "sdm_scan_workspace_size", "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
+        ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
+         "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
+         "sdm_status_str", "sdm_version"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -87,6 +88,35 @@ def test_score_topk_workspace_contract(L):
     assert score(L, d, ws=need, wsp=ctypes.c_void_p(0)) == 7
     assert score(L, d, ws=need, wsp=ctypes.c_void_p(4104)) == 5
     assert sdm.score_topk_workspace_size(2, 8, 4096, 128, 1024, 64, 64) == need
+
+
+def test_pack_and_packed_score_reject_before_any_launch(L):
+    d = dims(B=2, H=8, T=64, d_k=128, n_sub=1024, W=64, R=64)
+    need = L.sdm_score_topk_workspace_size(ctypes.byref(d), 1)
+    pack = lambda d, dt=1, sk=P, ws=need, wsp=P: L.sdm_pack_subkeys(
+        ctypes.byref(d), dt, sk, wsp, ctypes.c_size_t(ws), None)
+    assert L.sdm_pack_subkeys(None, 1, P, P, ctypes.c_size_t(need), None) == 1
+    assert pack(d, sk=ctypes.c_void_p(0)) == 1
+    assert pack(d, dt=4) == 3
+    assert pack(dims(d_k=40)) == 4
+    assert pack(d, sk=ctypes.c_void_p(4100)) == 5
+    assert pack(d, ws=need - 1) == 7
+    assert pack(d, wsp=ctypes.c_void_p(0)) == 7
+    assert pack(d, wsp=ctypes.c_void_p(4104)) == 5
+    # fp32 tables need no packing: accepted with no workspace and no launch
+    assert pack(d, dt=0, ws=0, wsp=ctypes.c_void_p(0)) == 0
+
+    def packed(d, ws=need, wsp=P, null_at=None):
+        args = [P] * 7
+        if null_at is not None:
+            args[null_at] = ctypes.c_void_p(0)
+        return L.sdm_score_topk_packed(ctypes.byref(d), 1, *args, wsp, ctypes.c_size_t(ws), None)
+    for i in range(7):
+        assert packed(d, null_at=i) == 1
+    assert packed(dims(W=33)) == 4
+    assert packed(d, ws=need - 1) == 7
+    assert packed(d, wsp=ctypes.c_void_p(0)) == 7
+    assert packed(d, wsp=ctypes.c_void_p(4104)) == 5
 
 
 def scan(L, d, dt=0, ptr=P, ws=0, null_at=None):
