@@ -53,7 +53,8 @@ def measured_scan_traffic(wl):
         return None
     rec = json.load(open(path))
     csrc = os.path.join(ROOT, "sparse_addressed_linear_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("scan.hip", "sdm_internal.h"))
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("scan.hip", "scan_common.h", "sdm_internal.h"))
     if rec.get("scan_source_sha256") != hashlib.sha256(src).hexdigest():
         return None
     return rec["hbm_bytes_per_launch"]

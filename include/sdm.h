@@ -174,6 +174,89 @@ int sdm_scan(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int32_t* w
 size_t sdm_scan_workspace_size(const sdm_dims* dims);
 
 /*
+ * Training: the gradients of the path (SDM is trained end to end, Spanish page
+ * "Resultados Experimentales", and its initial table M0 is a learned parameter,
+ * "Estado Inicial Aprendido").  The slot selections are piecewise constant, so
+ * these are the gradients with the forward's slots held fixed.  A training
+ * step runs sdm_score_topk, sdm_scan_record, then (with the loss gradient dout)
+ * sdm_scan_backward and sdm_score_topk_backward.
+ *
+ * sdm_scan_record -- sdm_scan that also stores, for every write event, the
+ * row as it was before the write:
+ *   tape     [B][H][T][W][d_v]  fp32  out: tape[b,h,t,r] = M_{t-1}[widx[b,h,t,r]]
+ * Everything else (arguments, workspace, limits, results) is sdm_scan's.
+ */
+int sdm_scan_record(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int32_t* widx,
+                    const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+                    const float* alpha, const float* beta, float* out, float* tape,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdm_scan_backward -- reverse sweep of the scan.  With L a loss, dout = dL/do
+ * and dM holding dL/dM_T on entry, it walks t = T-1..0 and for each token
+ * takes the read's adjoint, then the write's:
+ *   read:  drwt_r = <dout_t, M_t[ridx_r]>,  dM[ridx_r] += rwt_r * dout_t
+ *   write: G = dM[s_r], old = tape_t[r], c = beta_t * wwt_r,
+ *          dwwt_r = beta_t * <G, v_t - alpha_t old>,
+ *          dbeta_t = sum_r wwt_r <G, v_t - alpha_t old>,
+ *          dalpha_t = sum_r (1 - c) <G, old>,   dv_t = sum_r c G,
+ *          dM[s_r] = (1 - c) alpha_t G,   M[s_r] = old.
+ *
+ *   M        [B][H][N][d_v]  fp32  in: the table after the forward (the one
+ *                                  sdm_scan_record left); out: M0, restored
+ *   dM       [B][H][N][d_v]  fp32  in: dL/dM_T (zeros if the final table is
+ *                                  not used); out: dL/dM0
+ *   widx, wwt, ridx, rwt, v, alpha, beta   the forward's inputs, unchanged
+ *   tape     [B][H][T][W][d_v] fp32  from sdm_scan_record
+ *   dout     [B][H][T][d_v]  fp32
+ *   dv       [B][H][T][d_v]  fp32  out (fp32 whatever v_dtype is)
+ *   dalpha, dbeta [B][H][T]  fp32  out
+ *   dwwt     [B][H][T][W]    fp32  out: dL/dwwt
+ *   drwt     [B][H][T][R]    fp32  out: dL/drwt
+ *   workspace                       sdm_scan_backward_workspace_size(dims) bytes
+ *
+ * Results are deterministic.  The restored M equals M0 bit for bit (each
+ * written row gets back its recorded value).  Kernel limits (else
+ * SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256]; W, R <= 256.
+ */
+int sdm_scan_backward(const sdm_dims* dims, sdm_dtype v_dtype, float* M, float* dM,
+                      const int32_t* widx, const float* wwt, const int32_t* ridx,
+                      const float* rwt, const void* v, const float* alpha, const float* beta,
+                      const float* tape, const float* dout, float* dv, float* dalpha,
+                      float* dbeta, float* dwwt, float* drwt, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sdm_scan_backward needs (0 when none, or when
+ * the sizes are invalid or unsupported).  Pure host function. */
+size_t sdm_scan_backward_workspace_size(const sdm_dims* dims);
+
+/*
+ * sdm_score_topk_backward -- adjoint of the addressing (Spanish page
+ * "Mecanismo Central" item 2, softmax weights over the selected slot scores).
+ * For each token and each side (writes: k', widx, wwt, dwwt; reads: q', ridx,
+ * rwt, drwt), with slot s_r = i_r*n_sub + j_r:
+ *   dsigma_r = w_r (dw_r - sum_u w_u dw_u)
+ *   dx[0:d_k/2) = sum_r dsigma_r C[h][0][i_r],  dx[d_k/2:d_k) = sum_r dsigma_r C[h][1][j_r]
+ *   dsubkeys[h][0][i_r] += dsigma_r x[0:d_k/2),  dsubkeys[h][1][j_r] += dsigma_r x[d_k/2:d_k)
+ *
+ *   qp, kp, subkeys           in_dtype, as given to sdm_score_topk
+ *   widx, wwt, ridx, rwt      sdm_score_topk's outputs
+ *   dwwt, drwt                fp32 gradients of the weights (sdm_scan_backward's)
+ *   dq, dk    [B][H][T][d_k]  fp32 out (overwritten)
+ *   dsubkeys  [H][2][n_sub][d_k/2] fp32 in/out: the gradient is ADDED (the
+ *                             caller clears it, or accumulates over calls)
+ *
+ * dq and dk are deterministic; dsubkeys is summed with float atomics, so its
+ * last bits can differ between runs.  Kernel limits (else
+ * SDM_ERR_UNSUPPORTED): n_sub <= 1024, d_k/2 <= 256, W, R <= 128.
+ */
+int sdm_score_topk_backward(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp,
+                            const void* kp, const void* subkeys, const int32_t* widx,
+                            const float* wwt, const int32_t* ridx, const float* rwt,
+                            const float* dwwt, const float* drwt, float* dq, float* dk,
+                            float* dsubkeys, void* stream);
+
+/*
  * sdm_gdn_scan -- the dense gated DeltaNet recurrence that SDM extends
  * (Spanish page "Planteamiento del Problema", "Metodologia"; its state
  * starts at zero, "Estado Inicial Aprendido"), used as the IsoFLOP baseline:

@@ -24,8 +24,9 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE"
           4: "SDM_ERR_UNSUPPORTED", 5: "SDM_ERR_ALIGN", 6: "SDM_ERR_HIP",
           7: "SDM_ERR_WORKSPACE"}
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-           "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
-           "sdm_status_str", "sdm_version")
+           "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
+           "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
+           "sdm_gdn_scan", "sdm_status_str", "sdm_version")
 
 
 class SdmError(RuntimeError):
@@ -62,6 +63,14 @@ def lib():
         L.sdm_score_topk_workspace_size.restype = SZ
         L.sdm_scan.argtypes = [PD, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_scan.restype = ctypes.c_int
+        L.sdm_scan_record.argtypes = [PD, I32] + [P] * 11 + [SZ, P]
+        L.sdm_scan_record.restype = ctypes.c_int
+        L.sdm_scan_backward.argtypes = [PD, I32] + [P] * 17 + [SZ, P]
+        L.sdm_scan_backward.restype = ctypes.c_int
+        L.sdm_scan_backward_workspace_size.argtypes = [PD]
+        L.sdm_scan_backward_workspace_size.restype = SZ
+        L.sdm_score_topk_backward.argtypes = [PD, I32] + [P] * 13
+        L.sdm_score_topk_backward.restype = ctypes.c_int
         L.sdm_scan_workspace_size.argtypes = [PD]
         L.sdm_scan_workspace_size.restype = SZ
         L.sdm_gdn_scan.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
@@ -178,9 +187,12 @@ def scan_workspace_size(B, H, T, N, d_v, W, R):
     return int(lib().sdm_scan_workspace_size(ctypes.byref(d)))
 
 
-def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stream=None):
+def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stream=None,
+         tape=None):
     """Sparse gated-delta scan; M [B,H,N,d_v] fp32 is updated in place.
-    Returns out [B,H,T,d_v] fp32."""
+    Returns out [B,H,T,d_v] fp32.  With ``tape`` (fp32 [B,H,T,W,d_v]) the
+    pre-write row of every write event is recorded there (sdm_scan_record),
+    for scan_backward."""
     B, H, N, d_v = M.shape
     n_sub = int(round(N ** 0.5))
     if n_sub * n_sub != N:
@@ -199,14 +211,78 @@ def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stre
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=M.device)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
-    rc = lib().sdm_scan(ctypes.byref(d), dt, _dev(M, "M", torch.float32),
-                        _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", torch.float32),
-                        _dev(ridx, "ridx", torch.int32), _dev(rwt, "rwt", torch.float32),
-                        _dev(v, "v"), _dev(alpha, "alpha", torch.float32),
-                        _dev(beta, "beta", torch.float32), _dev(out, "out", torch.float32),
-                        wsp, ctypes.c_size_t(need), _stream(stream))
-    _check("sdm_scan", rc)
+    args = [_dev(M, "M", torch.float32), _dev(widx, "widx", torch.int32),
+            _dev(wwt, "wwt", torch.float32), _dev(ridx, "ridx", torch.int32),
+            _dev(rwt, "rwt", torch.float32), _dev(v, "v"), _dev(alpha, "alpha", torch.float32),
+            _dev(beta, "beta", torch.float32), _dev(out, "out", torch.float32)]
+    if tape is None:
+        rc = lib().sdm_scan(ctypes.byref(d), dt, *args, wsp, ctypes.c_size_t(need),
+                            _stream(stream))
+        _check("sdm_scan", rc)
+    else:
+        if tape.shape != (B, H, T, W, d_v):
+            raise ValueError("tape must be [B,H,T,W,d_v]")
+        rc = lib().sdm_scan_record(ctypes.byref(d), dt, *args, _dev(tape, "tape", torch.float32),
+                                   wsp, ctypes.c_size_t(need), _stream(stream))
+        _check("sdm_scan_record", rc)
     return out
+
+
+def scan_backward(M, dM, widx, wwt, ridx, rwt, v, alpha, beta, tape, dout, workspace=None,
+                  stream=None):
+    """Reverse sweep of the scan.  M: the table the recorded forward left
+    (restored to M0 in place); dM: dL/dM_T on entry, dL/dM0 on return (in
+    place).  Returns dict dv, dalpha, dbeta, dwwt, drwt (fp32)."""
+    B, H, N, d_v = M.shape
+    n_sub = int(round(N ** 0.5))
+    T, W = widx.shape[2], widx.shape[3]
+    R = ridx.shape[3]
+    if dM.shape != M.shape or tape.shape != (B, H, T, W, d_v) or dout.shape != (B, H, T, d_v):
+        raise ValueError("shape mismatch in scan_backward arguments")
+    dev = M.device
+    g = dict(dv=torch.empty((B, H, T, d_v), device=dev), dalpha=torch.empty((B, H, T), device=dev),
+             dbeta=torch.empty((B, H, T), device=dev), dwwt=torch.empty((B, H, T, W), device=dev),
+             drwt=torch.empty((B, H, T, R), device=dev))
+    d = Dims(B, H, T, 2, n_sub, d_v, W, R)
+    need = int(lib().sdm_scan_backward_workspace_size(ctypes.byref(d)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
+    f32 = torch.float32
+    rc = lib().sdm_scan_backward(
+        ctypes.byref(d), _dtype_code(v), _dev(M, "M", f32), _dev(dM, "dM", f32),
+        _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", f32), _dev(ridx, "ridx", torch.int32),
+        _dev(rwt, "rwt", f32), _dev(v, "v"), _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
+        _dev(tape, "tape", f32), _dev(dout, "dout", f32), _dev(g["dv"], "dv"),
+        _dev(g["dalpha"], "dalpha"), _dev(g["dbeta"], "dbeta"), _dev(g["dwwt"], "dwwt"),
+        _dev(g["drwt"], "drwt"), wsp, ctypes.c_size_t(need), _stream(stream))
+    _check("sdm_scan_backward", rc)
+    return g
+
+
+def score_topk_backward(qp, kp, subkeys, widx, wwt, ridx, rwt, dwwt, drwt, dsubkeys=None,
+                        stream=None):
+    """Adjoint of the addressing.  Returns (dq, dk, dsubkeys), fp32; the
+    sub-key gradient is added into ``dsubkeys`` when given (else a zeroed one)."""
+    B, H, T, d_k = qp.shape
+    n_sub = subkeys.shape[2]
+    W, R = widx.shape[3], ridx.shape[3]
+    dt = _dtype_code(qp, kp, subkeys)
+    dev = qp.device
+    dq = torch.empty((B, H, T, d_k), device=dev)
+    dk = torch.empty((B, H, T, d_k), device=dev)
+    if dsubkeys is None:
+        dsubkeys = torch.zeros(subkeys.shape, dtype=torch.float32, device=dev)
+    d = Dims(B, H, T, d_k, n_sub, 1, W, R)
+    f32 = torch.float32
+    rc = lib().sdm_score_topk_backward(
+        ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
+        _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", f32), _dev(ridx, "ridx", torch.int32),
+        _dev(rwt, "rwt", f32), _dev(dwwt, "dwwt", f32), _dev(drwt, "drwt", f32),
+        _dev(dq, "dq", f32), _dev(dk, "dk", f32), _dev(dsubkeys, "dsubkeys", f32),
+        _stream(stream))
+    _check("sdm_score_topk_backward", rc)
+    return dq, dk, dsubkeys
 
 
 def decode_step(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, bufs=None,

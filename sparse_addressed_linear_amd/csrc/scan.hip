@@ -52,35 +52,15 @@
 #include <stdint.h>
 
 #include "sdm_internal.h"
+#include "scan_common.h"
 
 namespace sdm {
+
+using namespace scanc;
 
 namespace {
 
 constexpr int kLevel = 0x7f;
-constexpr uint64_t kEmpty = 0x00000000ffffffffull;  // hash entry: key -1, no writers
-
-__device__ __forceinline__ uint32_t mix32(uint32_t x) {
-  x ^= x >> 16;
-  x *= 0x7feb352dU;
-  x ^= x >> 15;
-  x *= 0x846ca68bU;
-  x ^= x >> 16;
-  return x;
-}
-
-__device__ __forceinline__ float4 load_v4(const void* v, bool bf16, int64_t off) {
-  if (bf16) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(v) + off);
-    float4 r;
-    r.x = __uint_as_float(raw.x << 16);
-    r.y = __uint_as_float(raw.x & 0xffff0000u);
-    r.z = __uint_as_float(raw.y << 16);
-    r.w = __uint_as_float(raw.y & 0xffff0000u);
-    return r;
-  }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(v) + off);
-}
 
 // write strength c = beta*w and 1 - c, each rounded separately
 __device__ __forceinline__ void gate(float beta, float w, float& c, float& omc) {
@@ -104,38 +84,14 @@ __device__ __forceinline__ float4 upd4(float4 m, float a, float omc, float c, fl
                      upd(m.z, a, omc, c, v.z), upd(m.w, a, omc, c, v.w));
 }
 
-__device__ __forceinline__ float4 fma4(float w, float4 x, float4 acc) {
-  return make_float4(__fmaf_rn(w, x.x, acc.x), __fmaf_rn(w, x.y, acc.y),
-                     __fmaf_rn(w, x.z, acc.z), __fmaf_rn(w, x.w, acc.w));
-}
-
-__device__ __forceinline__ float4 shfl_xor4(float4 a, int m) {
-  return make_float4(__shfl_xor(a.x, m), __shfl_xor(a.y, m), __shfl_xor(a.z, m),
-                     __shfl_xor(a.w, m));
-}
-
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// writer mask of slot s in table h (0 when absent)
-__device__ __forceinline__ uint32_t probe(const uint64_t* h, int hmsk, int32_t s) {
-  int p = (int)(mix32((uint32_t)s) & (uint32_t)hmsk);
-  while (true) {
-    const uint64_t ent = h[p];
-    const int32_t k = (int32_t)(uint32_t)ent;
-    if (k == s) return (uint32_t)(ent >> 32);
-    if (k == -1) return 0u;
-    p = (p + 1) & hmsk;
-  }
-}
-
 }  // namespace
 
 // LPR: lanes per row slice (CW = 4*LPR columns).  NW: waves = tokens per block.
 // MC: 64-wide chunks of a token's index list (W, R <= 64*MC).  EPL: events per
-// lane group held in registers (a wave holds EPL*64/LPR events).
-template <int LPR, bool VBF16, int NW, int MC, int EPL>
+// lane group held in registers (a wave holds EPL*64/LPR events).  TAPE: also
+// store every write event's row as it was before the write (the values the
+// reverse sweep of the gradient needs) at tape[stream][t][rank].
+template <int LPR, bool VBF16, int NW, int MC, int EPL, bool TAPE>
 __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
   constexpr int GPW = 64 / LPR;    // lane groups per wave
   constexpr int CAPW = GPW * EPL;  // events per wave held in registers
@@ -177,6 +133,11 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
   int32_t* ml = lmeta + wave * a.lcap;
 
   auto row = [&](int32_t s) -> float* { return Mst + (int64_t)s * a.d_v; };
+  // pre-write row of write event e of this wave's token (row `trow` of [S*T])
+  auto record = [&](int64_t trow, int e, const float4& x) {
+    if constexpr (TAPE)
+      *reinterpret_cast<float4*>(a.tape + (trow * a.W + (ml[e] >> 8)) * a.d_v + c0) = x;
+  };
   auto in_part = [&](int32_t s) { return ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp; };
 
   // ---- index prefetch for one token (registers; unconditional loads) -----
@@ -211,6 +172,7 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
           const int pos = nw + __popcll(bal & below);
           sl[pos] = ps[c];
           wl[pos] = pw[c];
+          if constexpr (TAPE) ml[pos] = (c * 64 + lane) << 8;  // rank in the token's list
         }
         nw += __popcll(bal);
       }
@@ -304,7 +266,10 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
     for (int e = lane; e < nec; e += 64) {
       const uint32_t m = probe(htab, hmsk, sl[e]);
       const int lvl = __popc(m & (e < nwc ? wbefore : rbefore));
-      ml[e] = lvl;
+      if constexpr (TAPE)
+        ml[e] = e < nwc ? ((ml[e] & ~kLevel) | lvl) : lvl;
+      else
+        ml[e] = lvl;
       mylvl = max(mylvl, lvl);
     }
     wave_lds_sync();  // levels written by other lanes are read below
@@ -324,6 +289,7 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
           float c, omc;
           gate(beta, wl[e], c, omc);
           *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
+          record(trow, e, X[i]);
         }
       }
       if (maxL == 0) {
@@ -353,6 +319,7 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
             float c, omc;
             gate(beta, wl[e], c, omc);
             *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
+            record(trow, e, X[i]);
           }
         }
         __syncthreads();  // level-L stores before level-(L+1) loads
@@ -395,6 +362,7 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
               float c, omc;
               gate(beta, wl[e], c, omc);
               *reinterpret_cast<float4*>(row(sl[e])) = upd4(X[i], alpha, omc, c, vv);
+              record(trow, e, X[i]);
             }
           }
         }
@@ -443,7 +411,8 @@ __global__ void __launch_bounds__(256) sdm_partial_sum_kernel(const float* __res
 
 template <int LPR, bool VBF16, int NW, int MC, int EPL>
 static hipError_t launch_scan_t(const ScanArgs& a, size_t lds, hipStream_t stream) {
-  auto k = sdm_scan_kernel<LPR, VBF16, NW, MC, EPL>;
+  auto k = a.tape ? sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, true>
+                  : sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

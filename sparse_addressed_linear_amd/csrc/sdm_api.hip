@@ -135,14 +135,55 @@ size_t sdm_scan_workspace_size(const sdm_dims* d) {
   return sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R).work_bytes;
 }
 
-int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
-             const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
-             const float* alpha, const float* beta, float* out, void* workspace,
-             size_t workspace_bytes, void* stream) {
+int sdm_score_topk_backward(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
+                            const void* kp, const void* subkeys, const int32_t* widx,
+                            const float* wwt, const int32_t* ridx, const float* rwt,
+                            const float* dwwt, const float* drwt, float* dq, float* dk,
+                            float* dsubkeys, void* stream) {
+  if (!d || !subkeys || !dsubkeys) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (d->T > 0 && (!qp || !kp || !widx || !wwt || !ridx || !rwt || !dwwt || !drwt || !dq || !dk))
+    return SDM_ERR_NULL;
+  if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
+  const int dh = d->d_k / 2;
+  if (d->n_sub > 1024 || dh > 256 || d->W > 128 || d->R > 128 || d->W > d->n_sub * d->n_sub ||
+      sdm::score_bwd_lds_bytes(d->n_sub) > kMaxLds)
+    return SDM_ERR_UNSUPPORTED;
+  if (d->T == 0) return SDM_OK;
+  sdm::ScoreBwdArgs a{};
+  a.qp = qp;
+  a.kp = kp;
+  a.subkeys = subkeys;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.dwwt = dwwt;
+  a.drwt = drwt;
+  a.dq = dq;
+  a.dk = dk;
+  a.dsub = dsubkeys;
+  a.S = d->B * d->H;
+  a.H = d->H;
+  a.T = d->T;
+  a.d_k = d->d_k;
+  a.n_sub = d->n_sub;
+  a.W = d->W;
+  a.R = d->R;
+  hipError_t e = sdm::launch_score_bwd(a, in_dtype == SDM_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+static int run_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
+                    const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+                    const float* alpha, const float* beta, float* out, float* tape,
+                    bool want_tape, void* workspace, size_t workspace_bytes, void* stream) {
   if (!d || !M) return SDM_ERR_NULL;
   int rc = check_dims(d);
   if (rc) return rc;
-  if (d->T > 0 && (!widx || !wwt || !ridx || !rwt || !v || !alpha || !beta || !out))
+  if (d->T > 0 && (!widx || !wwt || !ridx || !rwt || !v || !alpha || !beta || !out ||
+                   (want_tape && !tape)))
     return SDM_ERR_NULL;
   if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
   if (d->d_v % 16 != 0 || d->d_v > 512 || d->W > 256 || d->R > 256) return SDM_ERR_UNSUPPORTED;
@@ -151,7 +192,8 @@ int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx
   if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
   if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
     return SDM_ERR_WORKSPACE;
-  if (!aligned16(M) || !aligned16(v) || !aligned16(out) || (p.work_bytes && !aligned16(workspace)))
+  if (!aligned16(M) || !aligned16(v) || !aligned16(out) ||
+      (p.work_bytes && !aligned16(workspace)) || (want_tape && !aligned16(tape)))
     return SDM_ERR_ALIGN;
   if (d->T == 0) return SDM_OK;
   sdm::ScanArgs a{};
@@ -165,6 +207,7 @@ int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx
   a.beta = beta;
   a.out = out;
   a.work = static_cast<float*>(workspace);
+  a.tape = want_tape ? tape : nullptr;
   a.N = N;
   a.S = d->B * d->H;
   a.T = d->T;
@@ -172,6 +215,82 @@ int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx
   a.W = d->W;
   a.R = d->R;
   hipError_t e = sdm::launch_scan(a, p, v_dtype == SDM_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
+int sdm_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
+             const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+             const float* alpha, const float* beta, float* out, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  return run_scan(d, v_dtype, M, widx, wwt, ridx, rwt, v, alpha, beta, out, nullptr, false,
+                  workspace, workspace_bytes, stream);
+}
+
+int sdm_scan_record(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
+                    const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
+                    const float* alpha, const float* beta, float* out, float* tape,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return run_scan(d, v_dtype, M, widx, wwt, ridx, rwt, v, alpha, beta, out, tape, true,
+                  workspace, workspace_bytes, stream);
+}
+
+// whole rows per workgroup: d_v = 4 * (lanes per row), a power of two up to 256
+static bool bwd_dv_ok(int d_v) { return d_v >= 16 && d_v <= 256 && (d_v & (d_v - 1)) == 0; }
+
+size_t sdm_scan_backward_workspace_size(const sdm_dims* d) {
+  if (!d || check_dims(d) != SDM_OK || !bwd_dv_ok(d->d_v)) return 0;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  return sdm::plan_scan_bwd(d->B * d->H, d->T, N, d->d_v, d->W, d->R).work_bytes;
+}
+
+int sdm_scan_backward(const sdm_dims* d, sdm_dtype v_dtype, float* M, float* dM,
+                      const int32_t* widx, const float* wwt, const int32_t* ridx,
+                      const float* rwt, const void* v, const float* alpha, const float* beta,
+                      const float* tape, const float* dout, float* dv, float* dalpha,
+                      float* dbeta, float* dwwt, float* drwt, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!d || !M || !dM) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (d->T > 0 && (!widx || !wwt || !ridx || !rwt || !v || !alpha || !beta || !tape || !dout ||
+                   !dv || !dalpha || !dbeta || !dwwt || !drwt))
+    return SDM_ERR_NULL;
+  if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
+  if (!bwd_dv_ok(d->d_v) || d->W > 256 || d->R > 256) return SDM_ERR_UNSUPPORTED;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  const sdm::ScanBwdPlan p = sdm::plan_scan_bwd(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
+  if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
+    return SDM_ERR_WORKSPACE;
+  if (!aligned16(M) || !aligned16(dM) || !aligned16(v) || !aligned16(tape) || !aligned16(dout) ||
+      !aligned16(dv) || (p.work_bytes && !aligned16(workspace)))
+    return SDM_ERR_ALIGN;
+  if (d->T == 0) return SDM_OK;
+  sdm::ScanBwdArgs a{};
+  a.M = M;
+  a.dM = dM;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.tape = tape;
+  a.dout = dout;
+  a.dv = dv;
+  a.dalpha = dalpha;
+  a.dbeta = dbeta;
+  a.dwwt = dwwt;
+  a.drwt = drwt;
+  a.work = static_cast<float*>(workspace);
+  a.N = N;
+  a.S = d->B * d->H;
+  a.T = d->T;
+  a.d_v = d->d_v;
+  a.W = d->W;
+  a.R = d->R;
+  hipError_t e = sdm::launch_scan_bwd(a, p, v_dtype == SDM_BF16, (hipStream_t)stream);
   return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
 }
 

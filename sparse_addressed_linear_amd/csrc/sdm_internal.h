@@ -77,10 +77,69 @@ struct ScanArgs {
   const float* beta;
   float* out;              // [S][T][d_v]
   float* work;             // [P][S][T][d_v] partial reads (P > 1)
+  float* tape;             // [S][T][W][d_v] pre-write rows, or nullptr (not recorded)
   int64_t N;
   int32_t S, T, d_v, W, R;
   int32_t CS, P, hsize, lcap, xcd_map;
 };
+
+// Adjoint of the addressing: weight gradients to dq', dk' and the sub-keys.
+struct ScoreBwdArgs {
+  const void* qp;          // [S][T][d_k]
+  const void* kp;
+  const void* subkeys;     // [H][2][n_sub][dh]
+  const int32_t* widx;     // [S][T][W]
+  const float* wwt;
+  const int32_t* ridx;     // [S][T][R]
+  const float* rwt;
+  const float* dwwt;       // [S][T][W]
+  const float* drwt;       // [S][T][R]
+  float* dq;               // [S][T][d_k]
+  float* dk;
+  float* dsub;             // [H][2][n_sub][dh], accumulated
+  int32_t S, H, T, d_k, n_sub, W, R;
+};
+
+hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, hipStream_t stream);
+size_t score_bwd_lds_bytes(int n_sub);
+
+// Reverse sweep of the scan (gradients).  Rows are whole (d_v = 4*LPR floats).
+struct ScanBwdArgs {
+  float* M;                // [S][N][d_v] in: table after the last token; out: M0
+  float* dM;               // [S][N][d_v] in: dL/dM_T; out: dL/dM_0
+  const int32_t* widx;     // [S][T][W]   forward's slots and weights
+  const float* wwt;
+  const int32_t* ridx;     // [S][T][R]
+  const float* rwt;
+  const void* v;           // [S][T][d_v]
+  const float* alpha;      // [S][T]
+  const float* beta;
+  const float* tape;       // [S][T][W][d_v] pre-write rows from the forward
+  const float* dout;       // [S][T][d_v]
+  float* dv;               // [S][T][d_v]
+  float* dalpha;           // [S][T]
+  float* dbeta;
+  float* dwwt;             // [S][T][W]
+  float* drwt;             // [S][T][R]
+  float* work;             // P > 1: [P][S][T][d_v] partial dv, then [P][S][T][2] dalpha, dbeta
+  int64_t N;
+  int32_t S, T, d_v, W, R;
+  int32_t P, hsize, lcap, xcd_map;
+};
+
+struct ScanBwdPlan {
+  int lpr;      // lanes per row (d_v / 4)
+  int P;        // slot partitions
+  int epl;      // events per lane group held in registers
+  int hsize;    // LDS hash size (power of two)
+  int lcap;     // per-wave event list capacity
+  size_t lds;
+  size_t work_bytes;
+};
+
+ScanBwdPlan plan_scan_bwd(int S, int T, int64_t N, int d_v, int W, int R);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, const ScanBwdPlan& p, bool vbf16,
+                           hipStream_t stream);
 
 struct ScanPlan {
   int lpr;      // lanes per row slice (slice = 4*lpr columns)

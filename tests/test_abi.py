@@ -27,8 +27,9 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-         "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_gdn_scan",
-         "sdm_status_str", "sdm_version"])
+         "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
+         "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
+         "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -174,3 +175,47 @@ def test_python_binding_requires_device_tensors():
     C = torch.zeros(1, 2, 32, 16)
     with pytest.raises(ValueError, match="device tensor"):
         sdm.score_topk(x, x, C, 8, 8)
+
+
+def test_gradient_entry_points_reject_before_any_launch(L):
+    d = dims(B=2, H=4, T=64, d_k=128, n_sub=256, d_v=64, W=32, R=32)
+    # sdm_scan_record: sdm_scan's checks plus the tape
+    rec = lambda d, tape=P, ws=1 << 30: L.sdm_scan_record(
+        ctypes.byref(d), 0, *([P] * 9), tape, P, ctypes.c_size_t(ws), None)
+    assert rec(d, tape=ctypes.c_void_p(0)) == 1
+    assert rec(d, tape=ctypes.c_void_p(4100)) == 5
+    assert rec(dims(d_v=20)) == 4
+    # sdm_scan_backward: 17 pointers
+    need = L.sdm_scan_backward_workspace_size(ctypes.byref(d))
+    assert need > 0  # 8 streams spread over slot partitions
+
+    def bwd(d, null_at=None, dt=0, ws=need, wsp=P, ptr=P):
+        args = [ptr] * 16
+        if null_at is not None:
+            args[null_at] = ctypes.c_void_p(0)
+        return L.sdm_scan_backward(ctypes.byref(d), dt, *args, wsp, ctypes.c_size_t(ws), None)
+    for i in range(16):
+        assert bwd(d, null_at=i) == 1, i
+    assert bwd(d, dt=3) == 3
+    assert bwd(dims(d_v=48)) == 4          # rows must be a power of two
+    assert bwd(dims(d_v=512)) == 4
+    assert bwd(d, ws=need - 1) == 7
+    assert bwd(d, wsp=ctypes.c_void_p(0)) == 7
+    assert bwd(d, ptr=ctypes.c_void_p(4100)) == 5
+    assert L.sdm_scan_backward_workspace_size(ctypes.byref(dims(d_v=48))) == 0
+    z = ctypes.c_void_p(0)
+    assert L.sdm_scan_backward(ctypes.byref(dims(T=0)), 0, P, P, *([z] * 14), z,
+                               ctypes.c_size_t(0), None) == 0
+
+    # sdm_score_topk_backward: 12 pointers
+    def sbwd(d, null_at=None, dt=1):
+        args = [P] * 12
+        if null_at is not None:
+            args[null_at] = ctypes.c_void_p(0)
+        return L.sdm_score_topk_backward(ctypes.byref(d), dt, *args, None)
+    for i in range(12):
+        assert sbwd(d, null_at=i) == 1, i
+    assert sbwd(d, dt=2) == 3
+    assert sbwd(dims(n_sub=2048, W=8)) == 4
+    assert sbwd(dims(n_sub=256, W=129, R=8)) == 4
+    assert sbwd(dims(d_k=31)) == 2
