@@ -227,6 +227,131 @@ def bench_decode(args, wl, dev):
     print(json.dumps(line), flush=True)
 
 
+def scan_bwd_bytes_per_token(wl):
+    """Algorithmic bytes of the reverse scan per stream-token: each read row
+    is read from M and read-modified-written in dM (3 row transfers), each
+    write row read-modified-written in dM, its tape row read and its M row
+    restored (4 row transfers)."""
+    return (3 * wl.R + 4 * wl.W) * wl.d_v * 4
+
+
+def cpu_baseline_train(wl, x, dout, n_streams):
+    """Oracle (single thread) training step on the first n_streams streams:
+    the C oracle's addressing, then the fp64 gradient oracle's scan forward
+    and reverse sweep and its addressing adjoint."""
+    import oracle
+    import synth
+    from oracle import backward as ob
+    tok, t_total = 0, 0.0
+    for s in range(n_streams):
+        b, h = divmod(s, wl.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        m0 = synth.to_numpy(x["m0_cpu"][s])
+        hq, hk, hv, ha, hb = (synth.to_numpy(x[n][sl]) for n in ("q", "k", "v", "alpha", "beta"))
+        hc = synth.to_numpy(x["subkeys"][h:h + 1])
+        hd = synth.to_numpy(dout[sl])
+        t0 = time.perf_counter()
+        r = oracle.score_topk(hq, hk, hc, wl.W, wl.R)
+        g = ob.scan_backward_stream(m0, r["widx"][0, 0], r["wwt"][0, 0], r["ridx"][0, 0],
+                                    r["rwt"][0, 0], hv[0, 0], ha[0, 0], hb[0, 0], hd[0, 0])
+        ob.score_backward(hq, hk, hc, r["widx"], r["ridx"], g["dwwt"][None, None],
+                          g["drwt"][None, None])
+        t_total += time.perf_counter() - t0
+        tok += wl.T
+    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_streams} of {wl.streams} streams x all {wl.T} tokens ({tok} "
+                      "stream-tokens): C oracle addressing, fp64 numpy scan forward, reverse "
+                      "sweep and addressing adjoint, single-threaded"}
+
+
+def bench_train(args, wl, dev):
+    """Training step: addressing, the scan recording its tape, the reverse scan
+    (which walks the table back to M0, so every step starts from the same
+    table) and the addressing adjoint.  The gradient of M0 and of the sub-keys
+    accumulate over the steps, as gradient buffers do; clearing them is the
+    optimiser's work and is not timed."""
+    import torch
+
+    import sparse_addressed_linear_amd as sdm
+    import synth
+    print(f"[bench] workload {wl.name} (training step): generating inputs on the device",
+          file=sys.stderr, flush=True)
+    x = synth.make_inputs(wl, device=dev)
+    B, H, T = wl.B, wl.H, wl.T
+    n_cpu = args.cpu_streams if args.cpu_streams is not None else \
+        {"tiny": 1, "mid": 4, "large": 2, "long": 1}[wl.name]
+    n_cpu = min(n_cpu, wl.streams)
+    x["m0_cpu"] = [x["m0"][s // H, s % H].cpu() for s in range(n_cpu)]
+    gen = torch.Generator(device=dev).manual_seed(wl.seed * 1000 + 99)
+    dout = torch.randn((B, H, T, wl.d_v), generator=gen, device=dev)
+    M = x["m0"]
+    dM = torch.zeros_like(M)
+    dC = torch.zeros(x["subkeys"].shape, dtype=torch.float32, device=dev)
+    tape = torch.empty((B, H, T, wl.W, wl.d_v), device=dev)
+    idx = (torch.empty((B, H, T, wl.W), dtype=torch.int32, device=dev),
+           torch.empty((B, H, T, wl.W), device=dev),
+           torch.empty((B, H, T, wl.R), dtype=torch.int32, device=dev),
+           torch.empty((B, H, T, wl.R), device=dev))
+    out = torch.empty((B, H, T, wl.d_v), device=dev)
+    need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
+    work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
+        sdm.score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R, out=idx)
+        rec(1)
+        sdm.scan(M, *idx, x["v"], x["alpha"], x["beta"], out=out, workspace=work, tape=tape)
+        rec(2)
+        g = sdm.scan_backward(M, dM, *idx, x["v"], x["alpha"], x["beta"], tape, dout)
+        rec(3)
+        sdm.score_topk_backward(x["q"], x["k"], x["subkeys"], *idx, g["dwwt"], g["drwt"],
+                                dsubkeys=dC)
+        rec(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} training steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    part = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(4)]
+    stream_tokens = wl.streams * T
+    bbytes = stream_tokens * scan_bwd_bytes_per_token(wl)
+    achieved = bbytes / (part[2] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": "sdm_scan_bwd (sdm_scan_bwd_kernel + sdm_bwd_sum_kernel)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "ms": round(part[2], 4), "bytes_per_launch": bbytes}
+    del tape
+    cpu = None
+    if n_cpu:
+        print(f"[bench] CPU baseline: oracle on {n_cpu} streams", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_train(wl, x, dout, n_cpu)
+    fwd_bytes = stream_tokens * (scan_bytes_per_token(wl) + wl.W * wl.d_v * 4)
+    cfg = {"workload": wl.name, "B": B, "H": H, "T": T, "d_k": wl.d_k, "d_v": wl.d_v,
+           "n_sub": wl.n_sub, "N": wl.N, "W": wl.W, "R": wl.R,
+           "inputs": "bf16" if wl.bf16 else "fp32", "table": "fp32",
+           "step": "addressing + recorded scan + reverse scan + addressing adjoint"}
+    line = {"metric": "SDM training step (forward + backward) stream-tokens/sec at N=2^20",
+            "value": round(stream_tokens / (ms_wall * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": cfg,
+            "roofline": roof, "cpu_baseline": cpu,
+            "kernels": {"score_topk_ms": round(part[0], 4),
+                        "scan_record_ms": round(part[1], 4),
+                        "scan_record_GBps": round(fwd_bytes / (part[1] * 1e-3) / 1e9, 1),
+                        "scan_backward_ms": round(part[2], 4),
+                        "score_topk_backward_ms": round(part[3], 4)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +359,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "mid", "large", "long", "gdn", "decode"])
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step (forward with tape + both backward calls)")
     ap.add_argument("--cpu-streams", type=int, default=None,
                     help="streams in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
@@ -269,6 +396,12 @@ def main():
     wl = synth.WORKLOADS[args.config]
     if wl.name == "decode":
         bench_decode(args, wl, dev)
+        return
+    if args.train:
+        if wl.dense:
+            print("bench.py: --train covers the sparse path only", file=sys.stderr)
+            sys.exit(2)
+        bench_train(args, wl, dev)
         return
 
     print(f"[bench] workload {wl.name}: generating inputs on the device", file=sys.stderr,

@@ -363,10 +363,11 @@ hipError_t launch_bwd_t(const ScanBwdArgs& a, size_t lds, hipStream_t stream) {
 ScanBwdPlan plan_scan_bwd(int S, int T, int64_t N, int d_v, int W, int R) {
   ScanBwdPlan p{};
   p.lpr = d_v / 4;
-  // partitions: about two workgroups per CU while a token keeps >= 8 events
-  // in each partition
+  // partitions: one workgroup per CU (a workgroup holds 8 waves of up to 225
+  // VGPRs, so a second one would not fit and would wait for a whole
+  // sequence), while a token keeps >= 8 events in each partition
   int P = 1;
-  while (P < 64 && (int64_t)S * (P * 2) <= 2 * kTargetWorkgroups && (W + R) / (P * 2) >= 8 &&
+  while (P < 64 && (int64_t)S * (P * 2) <= kTargetWorkgroups && (W + R) / (P * 2) >= 8 &&
          P * 2 <= N)
     P *= 2;
   p.P = P;

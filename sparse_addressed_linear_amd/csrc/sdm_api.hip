@@ -148,7 +148,7 @@ int sdm_score_topk_backward(const sdm_dims* d, sdm_dtype in_dtype, const void* q
   if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
   const int dh = d->d_k / 2;
   if (d->n_sub > 1024 || dh > 256 || d->W > 128 || d->R > 128 || d->W > d->n_sub * d->n_sub ||
-      sdm::score_bwd_lds_bytes(d->n_sub) > kMaxLds)
+      sdm::score_bwd_lds_bytes(d->W > d->R ? d->W : d->R) > kMaxLds)
     return SDM_ERR_UNSUPPORTED;
   if (d->T == 0) return SDM_OK;
   sdm::ScoreBwdArgs a{};

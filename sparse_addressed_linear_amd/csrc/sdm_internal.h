@@ -101,7 +101,7 @@ struct ScoreBwdArgs {
 };
 
 hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, hipStream_t stream);
-size_t score_bwd_lds_bytes(int n_sub);
+size_t score_bwd_lds_bytes(int kmax);  // kmax = max(W, R)
 
 // Reverse sweep of the scan (gradients).  Rows are whole (d_v = 4*LPR floats).
 struct ScanBwdArgs {
