@@ -67,7 +67,8 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int LPR, bool VBF16, int EPL>
+// MC: 64-wide chunks of a token's index lists (W, R <= 64*MC).
+template <int LPR, bool VBF16, int EPL, int MC>
 __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a) {
   constexpr int GPW = 64 / LPR;    // rows per wave instruction
   constexpr int CAPW = GPW * EPL;  // events per wave held in registers
@@ -109,6 +110,36 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
   __syncthreads();
   const int nblk = (a.T + kNW - 1) / kNW;
 
+  // ---- the next block's index lists, weights, gates, v and dO, one block
+  // ahead in registers (unconditional loads at clamped addresses) ----------
+  int32_t ps[MC], qs[MC];
+  float pw[MC], qw[MC];
+  float nal, nbe;
+  float4 nv, ndO;
+  auto prefetch = [&](int blk) {
+    const int tk = blk * kNW + (kNW - 1 - wave);
+    const bool ok = blk >= 0 && tk < a.T;
+    const int64_t tr = (int64_t)st * a.T + (ok ? tk : 0);
+#pragma unroll
+    for (int c = 0; c < MC; c++) {
+      if (c * 64 < a.W) {
+        const int i = c * 64 + lane < a.W ? c * 64 + lane : a.W - 1;
+        ps[c] = a.widx[tr * a.W + i];
+        pw[c] = a.wwt[tr * a.W + i];
+      }
+      if (c * 64 < a.R) {
+        const int i = c * 64 + lane < a.R ? c * 64 + lane : a.R - 1;
+        qs[c] = a.ridx[tr * a.R + i];
+        qw[c] = a.rwt[tr * a.R + i];
+      }
+    }
+    nal = a.alpha[tr];
+    nbe = a.beta[tr];
+    nv = load_v4(a.v, VBF16, tr * a.d_v + c0);
+    ndO = *reinterpret_cast<const float4*>(a.dout + tr * a.d_v + c0);
+  };
+  prefetch(nblk - 1);
+
   for (int b = nblk - 1; b >= 0; b--) {
     const int tok = b * kNW + (kNW - 1 - wave);  // wave 0: the block's latest token
     const bool valid = tok < a.T;
@@ -118,38 +149,43 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
     // ---- 1. this token's events of the partition: reads, then writes ------
     int nr = 0, nwr = 0;
     if (valid) {
-      for (int c = 0; c * 64 < a.R; c++) {
-        const int i = c * 64 + lane;
-        const int32_t s = i < a.R ? a.ridx[trow * a.R + i] : 0;
-        const bool f = i < a.R && in_part(s);
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          const int pos = nr + __popcll(bal & below);
-          sl[pos] = s;
-          wl[pos] = a.rwt[trow * a.R + i];
-          ml[pos] = i << 8;
+#pragma unroll
+      for (int c = 0; c < MC; c++) {
+        if (c * 64 < a.R) {
+          const int i = c * 64 + lane;
+          const bool f = i < a.R && in_part(qs[c]);
+          const uint64_t bal = __ballot(f);
+          if (f) {
+            const int pos = nr + __popcll(bal & below);
+            sl[pos] = qs[c];
+            wl[pos] = qw[c];
+            ml[pos] = i << 8;
+          }
+          nr += __popcll(bal);
         }
-        nr += __popcll(bal);
       }
-      for (int c = 0; c * 64 < a.W; c++) {
-        const int i = c * 64 + lane;
-        const int32_t s = i < a.W ? a.widx[trow * a.W + i] : 0;
-        const bool f = i < a.W && in_part(s);
-        const uint64_t bal = __ballot(f);
-        if (f) {
-          const int pos = nr + nwr + __popcll(bal & below);
-          sl[pos] = s;
-          wl[pos] = a.wwt[trow * a.W + i];
-          ml[pos] = (i << 8) | kWrite;
+#pragma unroll
+      for (int c = 0; c < MC; c++) {
+        if (c * 64 < a.W) {
+          const int i = c * 64 + lane;
+          const bool f = i < a.W && in_part(ps[c]);
+          const uint64_t bal = __ballot(f);
+          if (f) {
+            const int pos = nr + nwr + __popcll(bal & below);
+            sl[pos] = ps[c];
+            wl[pos] = pw[c];
+            ml[pos] = (i << 8) | kWrite;
+          }
+          nwr += __popcll(bal);
         }
-        nwr += __popcll(bal);
       }
     }
     const int nev = nr + nwr;
     wave_lds_sync();
-    const float al = a.alpha[trow], be = a.beta[trow];
-    const float4 vv = load_v4(a.v, VBF16, trow * a.d_v + c0);
-    const float4 dO = *reinterpret_cast<const float4*>(a.dout + trow * a.d_v + c0);
+    const float al = nal, be = nbe;
+    const float4 vv = nv;
+    const float4 dO = ndO;
+    prefetch(b - 1);  // in flight while this block is processed
 
     // ---- 2. hash: slot -> events of the block (bit 2*wave + kind) ---------
     for (int e = lane; e < nev; e += 64) {
@@ -348,9 +384,9 @@ __global__ void __launch_bounds__(256) sdm_bwd_sum_kernel(const float* __restric
   }
 }
 
-template <int LPR, bool VBF16, int EPL>
+template <int LPR, bool VBF16, int EPL, int MC>
 hipError_t launch_bwd_t(const ScanBwdArgs& a, size_t lds, hipStream_t stream) {
-  auto k = sdm_scan_bwd_kernel<LPR, VBF16, EPL>;
+  auto k = sdm_scan_bwd_kernel<LPR, VBF16, EPL, MC>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -395,19 +431,24 @@ hipError_t launch_scan_bwd(const ScanBwdArgs& a0, const ScanBwdPlan& p, bool vbf
   a.xcd_map = ((int64_t)a.S * a.P) % 8 == 0 ? 1 : 0;
   if (a.T == 0) return hipSuccess;
   hipError_t e;
-#define SDM_BWD_CASE(LPR_, EPL_)                                          \
-  if (p.lpr == LPR_ && p.epl == EPL_) {                                   \
-    e = vbf16 ? launch_bwd_t<LPR_, true, EPL_>(a, p.lds, stream)          \
-              : launch_bwd_t<LPR_, false, EPL_>(a, p.lds, stream);        \
+  const int kmax = a.W > a.R ? a.W : a.R;
+  const int mc = kmax <= 64 ? 1 : kmax <= 128 ? 2 : 4;
+#define SDM_BWD_CASE(LPR_, EPL_, MC_)                                     \
+  if (p.lpr == LPR_ && p.epl == EPL_ && mc == MC_) {                      \
+    e = vbf16 ? launch_bwd_t<LPR_, true, EPL_, MC_>(a, p.lds, stream)     \
+              : launch_bwd_t<LPR_, false, EPL_, MC_>(a, p.lds, stream);   \
   } else
+#define SDM_BWD_MC(LPR_, EPL_) \
+  SDM_BWD_CASE(LPR_, EPL_, 1) SDM_BWD_CASE(LPR_, EPL_, 2) SDM_BWD_CASE(LPR_, EPL_, 4)
 #define SDM_BWD_EPL(LPR_) \
-  SDM_BWD_CASE(LPR_, 4) SDM_BWD_CASE(LPR_, 8) SDM_BWD_CASE(LPR_, 12) SDM_BWD_CASE(LPR_, 16)
+  SDM_BWD_MC(LPR_, 4) SDM_BWD_MC(LPR_, 8) SDM_BWD_MC(LPR_, 12) SDM_BWD_MC(LPR_, 16)
   SDM_BWD_EPL(4)
   SDM_BWD_EPL(8)
   SDM_BWD_EPL(16)
   SDM_BWD_EPL(32)
   SDM_BWD_EPL(64) { return hipErrorInvalidValue; }
 #undef SDM_BWD_EPL
+#undef SDM_BWD_MC
 #undef SDM_BWD_CASE
   if (e != hipSuccess) return e;
   if (p.P > 1) {
