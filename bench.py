@@ -352,13 +352,94 @@ def bench_train(args, wl, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_raven(args, wl, dev):
+    """Routed slots with selective decay: one step is the router of every
+    token (write and read sides) and the scan that applies the decaying
+    writes and reads on the same table."""
+    import torch
+
+    import sparse_addressed_linear_amd as sdm
+    import synth
+    print(f"[bench] workload {wl.name}: generating inputs on the device", file=sys.stderr,
+          flush=True)
+    x = synth.make_inputs(wl, device=dev)
+    B, H, T = wl.B, wl.H, wl.T
+    n_cpu = min(args.cpu_streams if args.cpu_streams is not None else 2, wl.streams)
+    m0_cpu = [x["m0"][s // H, s % H].cpu() for s in range(n_cpu)]
+    out = torch.empty((B, H, T, wl.d_v), device=dev)
+    need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
+    work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        r = sdm.route_topk(x["zk"], x["zq"], x["a"], wl.W)
+        if ev:
+            ev[1].record(stream)
+        sdm.scan(x["m0"], *r, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_route = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_scan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    st = wl.streams * T
+    sbytes = st * scan_bytes_per_token(wl)
+    rbytes = st * (2 * wl.N * 4 + 4 + 4 * wl.W * 4)  # logits, decay, two (slot, value) lists
+    achieved = sbytes / (ms_scan * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
+    cpu = None
+    if n_cpu:
+        import numpy as np
+        from oracle import raven as rv
+        print(f"[bench] CPU baseline: oracle on {n_cpu} streams", file=sys.stderr, flush=True)
+        tok, tt = 0, 0.0
+        for s_ in range(n_cpu):
+            b, h = divmod(s_, H)
+            S = synth.to_numpy(m0_cpu[s_]).astype(np.float64)
+            zk, zq, a_ = (synth.to_numpy(x[n][b, h]) for n in ("zk", "zq", "a"))
+            u = x["v"][b, h].float().cpu().numpy().astype(np.float64)
+            t0 = time.perf_counter()
+            rv.raven_scan_stream(S, zk, zq, a_, u, wl.W)
+            tt += time.perf_counter() - t0
+            tok += T
+        cpu = {"value": tok / tt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_cpu} of {wl.streams} streams x all {T} tokens ({tok} "
+                         "stream-tokens), router + decaying writes + reads, fp64 numpy"}
+    cfg = {"workload": wl.name, "B": B, "H": H, "T": T, "M": wl.N, "K": wl.W, "d": wl.d_v,
+           "content": "bf16" if wl.bf16 else "fp32", "table": "fp32",
+           "table_GB": round(wl.table_bytes() / 1e9, 2)}
+    line = {"metric": "Routed selective-decay slots: stream-tokens/sec (router + scan)",
+            "value": round(st / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "kernels": {"route_ms": round(ms_route, 4),
+                        "route_GBps": round(rbytes / (ms_route * 1e-3) / 1e9, 1),
+                        "scan_ms": round(ms_scan, 4)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="large",
-                    choices=["tiny", "mid", "large", "long", "gdn", "decode"])
+                    choices=["tiny", "mid", "large", "long", "gdn", "decode", "raven"])
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with tape + both backward calls)")
     ap.add_argument("--cpu-streams", type=int, default=None,
@@ -396,6 +477,9 @@ def main():
     wl = synth.WORKLOADS[args.config]
     if wl.name == "decode":
         bench_decode(args, wl, dev)
+        return
+    if wl.keys == "route":
+        bench_raven(args, wl, dev)
         return
     if args.train:
         if wl.dense:

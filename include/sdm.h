@@ -257,6 +257,31 @@ int sdm_score_topk_backward(const sdm_dims* dims, sdm_dtype in_dtype, const void
                             float* dsubkeys, void* stream);
 
 /*
+ * sdm_route_topk -- router of routed-slot writes with selective decay (Spanish
+ * page "Resumen Tecnico: Raven", section 2.2), a second workload on the same
+ * table and scan.  Per token and side, over M slot logits z:
+ *   m = sigmoid(z); keep the K largest (selected on z: sigmoid is strictly
+ *   increasing; ties to the lower slot); r = m / (sum of the kept m);
+ *   write side: wcoef = 1 - exp(a_t * r)  (a_t <= 0; computed as -expm1);
+ *   read side:  rwt = r.
+ * Lists are in rank order (logit descending, slot ascending).  With them,
+ * sdm_scan(alpha = beta = 1, wwt = wcoef, rwt, v = u) applies the page's
+ * S[i] = exp(a r_i) S[i] + (1 - exp(a r_i)) u_t on the routed slots only and
+ * reads the query side's routed slots after the write.
+ *
+ *   zk, zq   [B][H][T][M]  fp32   write-side and read-side router logits
+ *   a        [B][H][T]     fp32   decay (<= 0)
+ *   widx     [B][H][T][K]  int32  out;  wcoef [B][H][T][K] fp32 out
+ *   ridx     [B][H][T][K]  int32  out;  rwt   [B][H][T][K] fp32 out
+ *
+ * Inputs must be finite.  Kernel limits (else SDM_ERR_UNSUPPORTED): M <= 8192,
+ * K <= 128.  For sdm_scan the table needs N = M = n_sub^2.
+ */
+int sdm_route_topk(int32_t B, int32_t H, int32_t T, int32_t M, int32_t K, const float* zk,
+                   const float* zq, const float* a, int32_t* widx, float* wcoef, int32_t* ridx,
+                   float* rwt, void* stream);
+
+/*
  * sdm_gdn_scan -- the dense gated DeltaNet recurrence that SDM extends
  * (Spanish page "Planteamiento del Problema", "Metodologia"; its state
  * starts at zero, "Estado Inicial Aprendido"), used as the IsoFLOP baseline:

@@ -26,7 +26,7 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE"
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
            "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
            "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
-           "sdm_gdn_scan", "sdm_status_str", "sdm_version")
+           "sdm_route_topk", "sdm_gdn_scan", "sdm_status_str", "sdm_version")
 
 
 class SdmError(RuntimeError):
@@ -71,6 +71,8 @@ def lib():
         L.sdm_scan_backward_workspace_size.restype = SZ
         L.sdm_score_topk_backward.argtypes = [PD, I32] + [P] * 13
         L.sdm_score_topk_backward.restype = ctypes.c_int
+        L.sdm_route_topk.argtypes = [I32] * 5 + [P] * 8
+        L.sdm_route_topk.restype = ctypes.c_int
         L.sdm_scan_workspace_size.argtypes = [PD]
         L.sdm_scan_workspace_size.restype = SZ
         L.sdm_gdn_scan.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]
@@ -321,6 +323,27 @@ def decode_step(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, bufs=None
                rwt.view(H, B, 1, R), v.view(H, B, 1, d_v), alpha.view(H, B, 1),
                beta.view(H, B, 1), out=bufs["out"], workspace=bufs.get("scan_ws"), stream=stream)
     return out.view(H, B, d_v)
+
+
+def route_topk(zk, zq, a, K, stream=None):
+    """Router of routed-slot writes: zk, zq [B,H,T,M] fp32 logits, a [B,H,T]
+    fp32 decay.  Returns (widx, wcoef, ridx, rwt), [B,H,T,K] each, for
+    ``scan(M, widx, wcoef, ridx, rwt, u, ones, ones)``."""
+    B, H, T, M = zk.shape
+    if zq.shape != zk.shape or a.shape != (B, H, T):
+        raise ValueError("shape mismatch in route_topk arguments")
+    dev = zk.device
+    widx = torch.empty((B, H, T, K), dtype=torch.int32, device=dev)
+    ridx = torch.empty((B, H, T, K), dtype=torch.int32, device=dev)
+    wcoef = torch.empty((B, H, T, K), dtype=torch.float32, device=dev)
+    rwt = torch.empty((B, H, T, K), dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    rc = lib().sdm_route_topk(B, H, T, M, K, _dev(zk, "zk", f32), _dev(zq, "zq", f32),
+                              _dev(a, "a", f32), _dev(widx, "widx", torch.int32),
+                              _dev(wcoef, "wcoef", f32), _dev(ridx, "ridx", torch.int32),
+                              _dev(rwt, "rwt", f32), _stream(stream))
+    _check("sdm_route_topk", rc)
+    return widx, wcoef, ridx, rwt
 
 
 def gdn_scan(S, k, q, v, alpha, beta, out=None, stream=None):

@@ -175,6 +175,28 @@ int sdm_score_topk_backward(const sdm_dims* d, sdm_dtype in_dtype, const void* q
   return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
 }
 
+int sdm_route_topk(int32_t B, int32_t H, int32_t T, int32_t M, int32_t K, const float* zk,
+                   const float* zq, const float* a, int32_t* widx, float* wcoef, int32_t* ridx,
+                   float* rwt, void* stream) {
+  if (B < 1 || H < 1 || T < 0 || M < 1 || K < 1 || K > M) return SDM_ERR_SHAPE;
+  if (T > 0 && (!zk || !zq || !a || !widx || !wcoef || !ridx || !rwt)) return SDM_ERR_NULL;
+  if (M > 8192 || K > 128 || sdm::route_lds_bytes(M, K) > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  if (T == 0) return SDM_OK;
+  sdm::RouteArgs r{};
+  r.zk = zk;
+  r.zq = zq;
+  r.a = a;
+  r.widx = widx;
+  r.wcoef = wcoef;
+  r.ridx = ridx;
+  r.rwt = rwt;
+  r.units = (int64_t)B * H * T;
+  r.M = M;
+  r.K = K;
+  hipError_t e = sdm::launch_route(r, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
 static int run_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
                     const float* wwt, const int32_t* ridx, const float* rwt, const void* v,
                     const float* alpha, const float* beta, float* out, float* tape,

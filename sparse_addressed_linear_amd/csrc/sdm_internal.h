@@ -83,6 +83,22 @@ struct ScanArgs {
   int32_t CS, P, hsize, lcap, xcd_map;
 };
 
+// Router of routed-slot writes (sigmoid top-K over M slot logits).
+struct RouteArgs {
+  const float* zk;         // [units][M] write-side logits
+  const float* zq;         // [units][M] read-side logits
+  const float* a;          // [units] decay (<= 0)
+  int32_t* widx;           // [units][K]
+  float* wcoef;            // [units][K] write strength 1 - exp(a*r)
+  int32_t* ridx;           // [units][K]
+  float* rwt;              // [units][K] read gates
+  int64_t units;           // stream-tokens
+  int32_t M, K;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+size_t route_lds_bytes(int M, int K);
+
 // Adjoint of the addressing: weight gradients to dq', dk' and the sub-keys.
 struct ScoreBwdArgs {
   const void* qp;          // [S][T][d_k]

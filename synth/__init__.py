@@ -21,6 +21,12 @@ configurations; N(mu, var) names a variance):
           head plus N(0, 0.1^2) noise (queries pick prototypes independently).
 * gdn   : dense gated-delta baseline, B=16 H=16 T=8192 d_k=d_v=128, fp32;
           k, q = g/|g| with g ~ N(0, I); v ~ N(0,1); gates as tiny; S0 = 0.
+* raven : routed slots with selective decay on the same table and scan:
+          B=8 H=8 T=4096, M=1024 slots (n_sub=32), K=32 routed slots per
+          token and side, rows of d=128 (key and value states side by side);
+          router logits zk, zq ~ N(0,1) fp32 [B,H,T,M]; decay
+          a = -softplus(N(0,1)); content u ~ N(0,1) bf16 (in v); the scan's
+          alpha and beta are 1; S0 ~ N(0, 0.01).
 * decode: serving batch of B=32 sequences x H=8 heads at large's per-stream
           shape and distributions, T=64 decoding steps of one token each;
           `decode_layout` gives the step-major, head-major tensors and
@@ -35,7 +41,8 @@ BASE_SEED = 1234
 
 # one id per drawn tensor, so each gets an independent generator
 _TENSOR_IDS = {"q": 1, "k": 2, "subkeys": 3, "v": 4, "alpha": 5, "beta": 6, "m0": 7,
-               "proto": 8, "proto_k": 9, "proto_q": 10, "noise_k": 11, "noise_q": 12}
+               "proto": 8, "proto_k": 9, "proto_q": 10, "noise_k": 11, "noise_q": 12,
+               "zk": 13, "zq": 14, "decay": 15}
 
 
 @dataclass(frozen=True)
@@ -90,6 +97,8 @@ WORKLOADS = {
                      R=128, bf16=True, m0_std=0.1, keys="proto"),
     "gdn": Workload("gdn", 4, B=16, H=16, T=8192, d_k=128, n_sub=0, d_v=128, W=0, R=0,
                     bf16=False, m0_std=0.0, dense=True),
+    "raven": Workload("raven", 6, B=8, H=8, T=4096, d_k=0, n_sub=32, d_v=128, W=32, R=32,
+                      bf16=True, m0_std=0.1, keys="route"),
     "decode": Workload("decode", 5, B=32, H=8, T=64, d_k=128, n_sub=1024, d_v=64, W=64, R=64,
                        bf16=True, m0_std=0.1, head_scale=(0.5, 2.0)),
 }
@@ -129,6 +138,19 @@ def make_inputs(wl: Workload, device="cpu", with_m0: bool = True) -> dict:
         out["s0"] = torch.zeros((B, H, wl.d_v, wl.d_k), device=device, dtype=torch.float32)
         return out
 
+    if wl.keys == "route":
+        M = wl.N
+        out["zk"] = _randn(wl, "zk", (B, H, T, M), device)
+        out["zq"] = _randn(wl, "zq", (B, H, T, M), device)
+        out["a"] = -torch.nn.functional.softplus(_randn(wl, "decay", (B, H, T), device))
+        out["alpha"] = torch.ones((B, H, T), device=device)
+        out["beta"] = torch.ones((B, H, T), device=device)
+        out["v"] = _randn(wl, "v", (B, H, T, wl.d_v), device)
+        if wl.bf16:
+            out["v"] = out["v"].to(torch.bfloat16)
+        if with_m0:
+            out["m0"] = make_m0(wl, device)
+        return out
     dh = wl.d_k // 2
     if wl.keys == "proto":
         proto = _randn(wl, "proto", (H, wl.n_proto, wl.d_k), device)

@@ -29,7 +29,7 @@ def test_header_declares_expected_entry_points():
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
          "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
          "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
-         "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
+         "sdm_route_topk", "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -219,3 +219,17 @@ def test_gradient_entry_points_reject_before_any_launch(L):
     assert sbwd(dims(n_sub=2048, W=8)) == 4
     assert sbwd(dims(n_sub=256, W=129, R=8)) == 4
     assert sbwd(dims(d_k=31)) == 2
+
+
+def test_route_topk_rejects_before_any_launch(L):
+    route = lambda B=1, H=1, T=4, M=64, K=8, null_at=None: L.sdm_route_topk(
+        B, H, T, M, K, *[ctypes.c_void_p(0) if i == null_at else P for i in range(7)], None)
+    for i in range(7):
+        assert route(null_at=i) == 1
+    assert route(K=65) == 2          # K > M
+    assert route(K=0) == 2
+    assert route(T=-1) == 2
+    assert route(M=16384, K=8) == 4
+    assert route(M=256, K=129) == 4
+    z = ctypes.c_void_p(0)
+    assert L.sdm_route_topk(1, 1, 0, 64, 8, *([z] * 7), None) == 0
