@@ -440,6 +440,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="large",
                     choices=["tiny", "mid", "large", "long", "gdn", "decode", "raven"])
+    ap.add_argument("--timeparallel", action="store_true",
+                    help="run the scan in its time-parallel form (sdm_scan_timeparallel)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with tape + both backward calls)")
     ap.add_argument("--cpu-streams", type=int, default=None,
@@ -519,8 +521,15 @@ def main():
                     torch.empty((B, H, T, wl.R), dtype=torch.int32, device=dev),
                     torch.empty((B, H, T, wl.R), device=dev))
         out = torch.empty((B, H, T, wl.d_v), device=dev)
-        need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
-        work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        if args.timeparallel:
+            import ctypes
+            d = sdm.Dims(B, H, T, 2, wl.n_sub, wl.d_v, wl.W, wl.R)
+            need = int(sdm.lib().sdm_scan_timeparallel_workspace_size(ctypes.byref(d)))
+            scan_fn = sdm.scan_timeparallel
+        else:
+            need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
+            scan_fn = sdm.scan
+        work = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
         def step(ev=None):
             if ev:
@@ -528,7 +537,7 @@ def main():
             sdm.score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R, out=idx_bufs)
             if ev:
                 ev[1].record(stream)
-            sdm.scan(M, *idx_bufs, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
+            scan_fn(M, *idx_bufs, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
             if ev:
                 ev[2].record(stream)
 
@@ -564,9 +573,12 @@ def main():
         ms_scan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
         sbytes = stream_tokens * scan_bytes_per_token(wl)
         achieved = sbytes / (ms_scan * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)",
+        kname = ("sdm_scan_timeparallel (event keys, radix sort, slot segments, read sums)"
+                 if args.timeparallel else "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)")
+        roof = {"bound": "hbm", "kernel": kname,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_scan_traffic(wl),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if args.timeparallel else measured_scan_traffic(wl),
                 "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
         allb = stream_tokens * (scan_bytes_per_token(wl) + score_bytes_per_token(wl))
         kernels = {"score_topk_ms": round(ms_score, 4), "scan_ms": round(ms_scan, 4),
@@ -578,6 +590,8 @@ def main():
         cpu = cpu_baseline_gdn(wl, x, n_cpu) if dense else cpu_baseline(wl, x, n_cpu)
 
     cfg = {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d_k": wl.d_k, "d_v": wl.d_v}
+    if args.timeparallel:
+        cfg["scan"] = "time-parallel"
     if not dense:
         cfg.update({"n_sub": wl.n_sub, "N": wl.N, "W": wl.W, "R": wl.R,
                     "inputs": "bf16" if wl.bf16 else "fp32", "table": "fp32",

@@ -174,6 +174,36 @@ int sdm_scan(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int32_t* w
 size_t sdm_scan_workspace_size(const sdm_dims* dims);
 
 /*
+ * sdm_scan_timeparallel -- the same scan as sdm_scan, evaluated slot by slot
+ * instead of token by token.  Rows never interact: a row sees exactly the
+ * write and read events that name it, in time order (a token's write of a
+ * slot before its read of it).  The events of every stream are sorted by
+ * (slot, time); each touched row is then loaded once, its writes applied in
+ * time order, the row it holds at each read recorded, and each token's output
+ * summed over its reads in rank order.  The parallelism is the number of
+ * touched rows, not the number of streams.
+ *
+ * Arguments, layouts and results as sdm_scan, with this workspace:
+ *   workspace  sdm_scan_timeparallel_workspace_size(dims) bytes, 256-byte
+ *              aligned: sort keys and payloads (24 bytes per event, events =
+ *              B*H*T*(W+R)), the sort's scratch and a read buffer of
+ *              B*H*T*R*d_v floats.
+ * The table and the outputs are bit-identical to the sequential scan's
+ * definition (each element's fp32 operations in the same order).  Kernel
+ * limits (else SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256];
+ * B*H, N and T together within a 64-bit sort key; T*(W+R) < 2^32.
+ */
+int sdm_scan_timeparallel(const sdm_dims* dims, sdm_dtype v_dtype, float* M,
+                          const int32_t* widx, const float* wwt, const int32_t* ridx,
+                          const float* rwt, const void* v, const float* alpha,
+                          const float* beta, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sdm_scan_timeparallel needs (0 when the sizes
+ * are invalid or unsupported).  Pure host function. */
+size_t sdm_scan_timeparallel_workspace_size(const sdm_dims* dims);
+
+/*
  * Training: the gradients of the path (SDM is trained end to end, Spanish page
  * "Resultados Experimentales", and its initial table M0 is a learned parameter,
  * "Estado Inicial Aprendido").  The slot selections are piecewise constant, so

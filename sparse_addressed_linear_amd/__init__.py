@@ -26,7 +26,8 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE"
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
            "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
            "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
-           "sdm_route_topk", "sdm_gdn_scan", "sdm_status_str", "sdm_version")
+           "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
+           "sdm_gdn_scan", "sdm_status_str", "sdm_version")
 
 
 class SdmError(RuntimeError):
@@ -71,6 +72,10 @@ def lib():
         L.sdm_scan_backward_workspace_size.restype = SZ
         L.sdm_score_topk_backward.argtypes = [PD, I32] + [P] * 13
         L.sdm_score_topk_backward.restype = ctypes.c_int
+        L.sdm_scan_timeparallel.argtypes = [PD, I32] + [P] * 10 + [SZ, P]
+        L.sdm_scan_timeparallel.restype = ctypes.c_int
+        L.sdm_scan_timeparallel_workspace_size.argtypes = [PD]
+        L.sdm_scan_timeparallel_workspace_size.restype = SZ
         L.sdm_route_topk.argtypes = [I32] * 5 + [P] * 8
         L.sdm_route_topk.restype = ctypes.c_int
         L.sdm_scan_workspace_size.argtypes = [PD]
@@ -227,6 +232,35 @@ def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stre
         rc = lib().sdm_scan_record(ctypes.byref(d), dt, *args, _dev(tape, "tape", torch.float32),
                                    wsp, ctypes.c_size_t(need), _stream(stream))
         _check("sdm_scan_record", rc)
+    return out
+
+
+def scan_timeparallel(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None,
+                      stream=None):
+    """The scan evaluated slot by slot (sdm_scan_timeparallel): same arguments
+    and results as ``scan``; ``workspace`` (uint8, 256-byte aligned) is
+    allocated here when not given or too small."""
+    B, H, N, d_v = M.shape
+    n_sub = int(round(N ** 0.5))
+    T, W = widx.shape[2], widx.shape[3]
+    R = ridx.shape[3]
+    if widx.shape[:2] != (B, H) or ridx.shape[:3] != (B, H, T) or v.shape != (B, H, T, d_v) \
+            or alpha.shape != (B, H, T) or beta.shape != (B, H, T) or \
+            wwt.shape != widx.shape or rwt.shape != ridx.shape:
+        raise ValueError("shape mismatch in scan_timeparallel arguments")
+    if out is None:
+        out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
+    d = Dims(B, H, T, 2, n_sub, d_v, W, R)
+    need = int(lib().sdm_scan_timeparallel_workspace_size(ctypes.byref(d)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=M.device)
+    f32 = torch.float32
+    rc = lib().sdm_scan_timeparallel(
+        ctypes.byref(d), _dtype_code(v), _dev(M, "M", f32), _dev(widx, "widx", torch.int32),
+        _dev(wwt, "wwt", f32), _dev(ridx, "ridx", torch.int32), _dev(rwt, "rwt", f32),
+        _dev(v, "v"), _dev(alpha, "alpha", f32), _dev(beta, "beta", f32), _dev(out, "out", f32),
+        _dev(workspace, "workspace"), ctypes.c_size_t(need), _stream(stream))
+    _check("sdm_scan_timeparallel", rc)
     return out
 
 

@@ -256,6 +256,61 @@ int sdm_scan_record(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_
                   workspace, workspace_bytes, stream);
 }
 
+// time-parallel scan: whole rows per lane group, keys (stream, slot, t, kind)
+// in 64 bits, payload t*(W+R)+j in 32
+static int tp_shape_ok(const sdm_dims* d) {
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  const bool dv_ok = d->d_v >= 16 && d->d_v <= 256 && (d->d_v & (d->d_v - 1)) == 0;
+  if (!dv_ok || sdm::tp_key_bits(d->B * d->H, d->T, N) > 64 ||
+      (int64_t)d->T * (d->W + d->R) >= (int64_t{1} << 32))
+    return SDM_ERR_UNSUPPORTED;
+  return SDM_OK;
+}
+
+size_t sdm_scan_timeparallel_workspace_size(const sdm_dims* d) {
+  if (!d || check_dims(d) != SDM_OK || tp_shape_ok(d) != SDM_OK) return 0;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  return sdm::tp_workspace_bytes(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
+}
+
+int sdm_scan_timeparallel(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_t* widx,
+                          const float* wwt, const int32_t* ridx, const float* rwt,
+                          const void* v, const float* alpha, const float* beta, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d || !M) return SDM_ERR_NULL;
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (d->T > 0 && (!widx || !wwt || !ridx || !rwt || !v || !alpha || !beta || !out))
+    return SDM_ERR_NULL;
+  if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
+  rc = tp_shape_ok(d);
+  if (rc) return rc;
+  if (d->T == 0) return SDM_OK;
+  const int64_t N = (int64_t)d->n_sub * d->n_sub;
+  const size_t need = sdm::tp_workspace_bytes(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
+  if (!workspace || workspace_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(M) || !aligned16(v) || !aligned16(out) || (((uintptr_t)workspace) & 255))
+    return SDM_ERR_ALIGN;
+  sdm::TpArgs a{};
+  a.M = M;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.N = N;
+  a.S = d->B * d->H;
+  a.T = d->T;
+  a.d_v = d->d_v;
+  a.W = d->W;
+  a.R = d->R;
+  hipError_t e = sdm::launch_scan_tp(a, v_dtype == SDM_BF16, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
 // whole rows per workgroup: d_v = 4 * (lanes per row), a power of two up to 256
 static bool bwd_dv_ok(int d_v) { return d_v >= 16 && d_v <= 256 && (d_v & (d_v - 1)) == 0; }
 

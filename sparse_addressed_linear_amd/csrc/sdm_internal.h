@@ -83,6 +83,25 @@ struct ScanArgs {
   int32_t CS, P, hsize, lcap, xcd_map;
 };
 
+// Time-parallel form of the scan (events sorted by slot, then time).
+struct TpArgs {
+  float* M;                // [S][N][d_v] in/out
+  const int32_t* widx;     // [S][T][W]
+  const float* wwt;
+  const int32_t* ridx;     // [S][T][R]
+  const float* rwt;
+  const void* v;           // [S][T][d_v]
+  const float* alpha;      // [S][T]
+  const float* beta;
+  float* out;              // [S][T][d_v]
+  int64_t N;
+  int32_t S, T, d_v, W, R;
+};
+
+int tp_key_bits(int S, int T, int64_t N);
+size_t tp_workspace_bytes(int S, int T, int64_t N, int d_v, int W, int R);
+hipError_t launch_scan_tp(const TpArgs& a, bool vbf16, void* ws, hipStream_t stream);
+
 // Router of routed-slot writes (sigmoid top-K over M slot logits).
 struct RouteArgs {
   const float* zk;         // [units][M] write-side logits

@@ -29,7 +29,8 @@ def test_header_declares_expected_entry_points():
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
          "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
          "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
-         "sdm_route_topk", "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
+         "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
+         "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -233,3 +234,25 @@ def test_route_topk_rejects_before_any_launch(L):
     assert route(M=256, K=129) == 4
     z = ctypes.c_void_p(0)
     assert L.sdm_route_topk(1, 1, 0, 64, 8, *([z] * 7), None) == 0
+
+
+def test_scan_timeparallel_rejects_before_any_launch(L):
+    d = dims(B=2, H=4, T=64, d_k=128, n_sub=256, d_v=64, W=32, R=32)
+    need = L.sdm_scan_timeparallel_workspace_size(ctypes.byref(d))
+    # keys and payloads (24 bytes per event) plus the read buffer, at least
+    assert need >= 2 * 4 * 64 * 64 * 24 + 2 * 4 * 64 * 32 * 64 * 4
+
+    def tp(d, null_at=None, dt=0, ws=need, wsp=ctypes.c_void_p(4096), ptr=P):
+        args = [ptr] * 9
+        if null_at is not None:
+            args[null_at] = ctypes.c_void_p(0)
+        return L.sdm_scan_timeparallel(ctypes.byref(d), dt, *args, wsp, ctypes.c_size_t(ws), None)
+    for i in range(9):
+        assert tp(d, null_at=i) == 1, i
+    assert tp(d, dt=2) == 3
+    assert tp(dims(d_v=48)) == 4
+    assert tp(dims(d_v=512)) == 4
+    assert tp(d, ws=need - 1) == 7
+    assert tp(d, wsp=ctypes.c_void_p(0)) == 7
+    assert tp(d, wsp=ctypes.c_void_p(4112)) == 5   # not 256-byte aligned
+    assert L.sdm_scan_timeparallel_workspace_size(ctypes.byref(dims(d_v=48))) == 0
