@@ -82,33 +82,56 @@ __global__ void __launch_bounds__(256) sdm_tp_segments_kernel(TpArgs a, const ui
     const uint64_t prev = seg(keys[i - 1]);
     while (i < end && seg(keys[i]) == prev) i++;
   }
-  while (i < end) {
-    const uint64_t s0 = seg(keys[i]);
-    const int64_t st = (int64_t)(s0 >> nb);
-    const int64_t slot = (int64_t)(s0 & ((uint64_t{1} << nb) - 1));
-    float* row = a.M + (st * a.N + slot) * a.d_v + c0;
-    float4 m = *reinterpret_cast<const float4*>(row);
-    int64_t j = i;
-    do {
-      const uint32_t p = vals[j];
-      const int t = (int)(p / WR), r = (int)(p - (uint32_t)t * WR);
-      const int64_t tok = st * a.T + t;
-      if (r < a.W) {
-        const float c = a.beta[tok] * a.wwt[tok * a.W + r];
-        const float omc = 1.0f - c;
-        const float al = a.alpha[tok];
-        const float4 v = load_v4(a.v, VBF16, tok * a.d_v + c0);
-        m.x = omc * (al * m.x) + c * v.x;
-        m.y = omc * (al * m.y) + c * v.y;
-        m.z = omc * (al * m.z) + c * v.z;
-        m.w = omc * (al * m.w) + c * v.w;
-      } else {
-        *reinterpret_cast<float4*>(readbuf + (tok * a.R + (r - a.W)) * a.d_v + c0) = m;
-      }
-      j++;
-    } while (j < n && seg(keys[j]) == s0);
-    *reinterpret_cast<float4*>(row) = m;
-    i = j;
+  if (i >= end) return;
+  // keys and payloads two events ahead: the next segment's row and this
+  // event's gates and v are in flight together
+  auto rowp = [&](uint64_t sg) {
+    const int64_t st = (int64_t)(sg >> nb);
+    const int64_t slot = (int64_t)(sg & ((uint64_t{1} << nb) - 1));
+    return a.M + (st * a.N + slot) * a.d_v + c0;
+  };
+  uint64_t scur = seg(keys[i]);
+  uint32_t pj = vals[i];
+  bool more1 = i + 1 < n;
+  uint64_t k1 = more1 ? keys[i + 1] : ~uint64_t{0};
+  uint32_t p1 = more1 ? vals[i + 1] : 0u;
+  float* row = rowp(scur);
+  float4 m = *reinterpret_cast<const float4*>(row);
+  for (int64_t j = i;; j++) {
+    const bool more2 = j + 2 < n;
+    const uint64_t k2 = more2 ? keys[j + 2] : ~uint64_t{0};
+    const uint32_t p2 = more2 ? vals[j + 2] : 0u;
+    const uint64_t s1 = seg(k1);
+    const bool ends = !more1 || s1 != scur;         // event j closes its segment
+    const bool next_here = more1 && ends && j + 1 < end;  // and the next one is ours
+    float* row1 = next_here ? rowp(s1) : row;
+    const float4 mnext = *reinterpret_cast<const float4*>(row1);  // (row itself if unused)
+    const int64_t st = (int64_t)(scur >> nb);
+    const int t = (int)(pj / WR), r = (int)(pj - (uint32_t)t * WR);
+    const int64_t tok = st * a.T + t;
+    if (r < a.W) {
+      const float c = a.beta[tok] * a.wwt[tok * a.W + r];
+      const float omc = 1.0f - c;
+      const float al = a.alpha[tok];
+      const float4 v = load_v4(a.v, VBF16, tok * a.d_v + c0);
+      m.x = omc * (al * m.x) + c * v.x;
+      m.y = omc * (al * m.y) + c * v.y;
+      m.z = omc * (al * m.z) + c * v.z;
+      m.w = omc * (al * m.w) + c * v.w;
+    } else {
+      *reinterpret_cast<float4*>(readbuf + (tok * a.R + (r - a.W)) * a.d_v + c0) = m;
+    }
+    if (ends) {
+      *reinterpret_cast<float4*>(row) = m;
+      if (!next_here) break;  // no more events, or the next segment is the next chunk's
+      scur = s1;
+      row = row1;
+      m = mnext;
+    }
+    pj = p1;
+    more1 = more2;
+    k1 = k2;
+    p1 = p2;
   }
 }
 
