@@ -5,9 +5,10 @@ with T = 1, laid out head-major so that the tokens of one head score together.
 Rules:
   * stepping T tokens one call at a time gives the same bits as one call over
     the whole sequence: slot lists, weights, outputs and the final table;
-  * sampled streams match the oracle by the rules of the sequence tests (slot
-    sets modulo the gap rule, weights and outputs within 1e-5 + 1e-4|ref|, the
-    table bit-identical when the oracle's scan is fed the GPU's slots).
+  * sampled streams match the oracle by the rules of the sequence tests: slot
+    sets modulo the gap rule, weights within 1e-5 + 1e-4|ref|, and end to end
+    (the oracle's own addressing and scan) table and outputs within
+    1e-5 + 1e-4|ref| for streams with no flagged token.
 """
 import numpy as np
 import pytest
@@ -68,21 +69,26 @@ def test_decode_steps_equal_sequence_call(dev, use_packed):
         assert torch.equal(idx[j].permute(2, 1, 0, 3), g[j]), f"slot list {j} differs"
     assert torch.equal(outs.permute(2, 1, 0, 3), out_seq)
     assert torch.equal(M_dec.transpose(0, 1), M_seq)
-    # two sampled streams against the oracle, end to end from M0
+    # two sampled streams against the oracle's own addressing and scan, end to
+    # end from M0 (a stream holding a token flagged by the gap rule is skipped)
     for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
                                 wl.W, wl.R)
+        flags = 0
         for j, (ri, rw, gp) in enumerate(((ref["widx"], ref["wwt"], ref["wgap"]),
                                            (ref["ridx"], ref["rwt"], ref["rgap"]))):
             n, flagged, bad = compare_topk(np_(g[2 * j][sl]), np_(g[2 * j + 1][sl]), ri, rw, gp,
                                            wl.N)
             assert bad == 0
-        # the oracle's scan fed the decode path's slots: bit-identical table
+            flags += flagged
         M_ref = np.ascontiguousarray(M0_host[b:b + 1, h:h + 1])
-        o_ref = oracle.scan(M_ref, np_(g[0][sl]), np_(g[1][sl]), np_(g[2][sl]), np_(g[3][sl]),
+        o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
                             np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
-        assert np.array_equal(np_(M_dec[h, b]), M_ref[0, 0])
+        if flags:
+            say(f"  stream ({b},{h}) holds a flagged token; end to end not compared")
+            continue
+        assert np.all(close(np_(M_dec[h, b]), M_ref[0, 0]))
         assert np.all(close(np_(outs[:, h, b]), o_ref[0, 0]))
 
 
@@ -103,14 +109,20 @@ def test_decode_full_size_sampled(dev):
         ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
                                 wl.W, wl.R)
         gi = [np_(idx[j][:, h, b])[None, None] for j in range(4)]
+        flags = 0
         for j, (ri, rw, gp) in enumerate(((ref["widx"], ref["wwt"], ref["wgap"]),
                                            (ref["ridx"], ref["rwt"], ref["rgap"]))):
             n, flagged, bad = compare_topk(gi[2 * j], gi[2 * j + 1], ri, rw, gp, wl.N)
             say(f"  stream ({b},{h}) {'WR'[j]}: {n} tokens, {flagged} flagged, {bad} mismatched")
             assert bad == 0
+            flags += flagged
+        # end to end against the oracle's own addressing and scan
         M_ref = np.ascontiguousarray(M0[(b, h)][None, None])
-        o_ref = oracle.scan(M_ref, *gi, np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
-        assert np.array_equal(np_(M[h, b]), M_ref[0, 0])
+        o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
+                            np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
+        if flags:
+            continue
+        assert np.all(close(np_(M[h, b]), M_ref[0, 0]))
         assert np.all(close(np_(outs[:, h, b]), o_ref[0, 0]))
     del M
     torch.cuda.empty_cache()
