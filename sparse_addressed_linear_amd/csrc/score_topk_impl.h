@@ -153,40 +153,65 @@ __device__ uint64_t find_threshold(const uint64_t (&key)[NPL], int k, int cap, u
 }
 
 // Ascending-index bitonic network over 64*E keys held E per lane (element
-// i = lane*E + r), sorting into DESCENDING order.
-template <int E>
-__device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int lane) {
+// i = lane*E + r), sorting into DESCENDING order.  Stage S, step J are template
+// parameters, so each step's lane pattern (which lanes keep the larger key of
+// an exchange) is a compile-time 64-bit constant that becomes the select
+// condition directly (inverse ballot): no per-lane arithmetic, and nothing
+// for the register allocator to keep live (or spill) across the network.
+constexpr uint64_t keep_max_lanes(int E, int J, int S) {
+  // lanes whose element keeps the larger key of a cross-lane exchange: the
+  // lower slot of a descending run or the upper slot of an ascending one
+  // (J, S >= E, so the register index r does not change either bit)
+  uint64_t m = 0;
+  for (int l = 0; l < 64; l++) {
+    const int i = l * E;
+    if (((i & J) == 0) == ((i & S) == 0)) m |= 1ull << l;
+  }
+  return m;
+}
+
+constexpr uint64_t desc_lanes(int E, int r, int S) {  // element lane*E + r in a descending run
+  uint64_t m = 0;
+  for (int l = 0; l < 64; l++)
+    if (((l * E + r) & S) == 0) m |= 1ull << l;
+  return m;
+}
+
+template <typename K, int E, int S, int J>
+__device__ __forceinline__ void bitonic_step(K (&v)[E], int lane) {
+  if constexpr (J >= E) {
+    constexpr uint64_t km_bits = keep_max_lanes(E, J, S);
+    const bool km = __builtin_amdgcn_inverse_ballot_w64(km_bits);
 #pragma unroll
-  for (int s = 2; s <= 64 * E; s <<= 1) {
+    for (int r = 0; r < E; r++) {
+      const K o = xor_shuffle(v[r], J / E, lane);
+      // equal keys are equal values, so one compare decides
+      v[r] = ((o > v[r]) == km) ? o : v[r];
+    }
+  } else {
 #pragma unroll
-    for (int j = s >> 1; j > 0; j >>= 1) {
-      if (j >= E) {
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-          const uint64_t o = xor_shuffle(v[r], j / E, lane);
-          const int i = lane * E + r;
-          const bool lower = (i & j) == 0;
-          const bool desc = (i & s) == 0;
-          // keep the larger of the pair in the lower slot of a descending run
-          // (and in the upper slot of an ascending one); equal keys are equal
-          // values, so one compare decides
-          v[r] = ((o > v[r]) == (lower == desc)) ? o : v[r];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-          if ((r & j) == 0) {
-            const int i = lane * E + r;
-            const bool desc = (i & s) == 0;
-            const uint64_t p = v[r], q = v[r | j];
-            const bool swap = (q > p) == desc;  // equal keys: swapping changes nothing
-            v[r] = swap ? q : p;
-            v[r | j] = swap ? p : q;
-          }
-        }
+    for (int r = 0; r < E; r++) {
+      if ((r & J) == 0) {
+        const bool desc = __builtin_amdgcn_inverse_ballot_w64(desc_lanes(E, r, S));
+        const K p = v[r], q = v[r | J];
+        const bool swap = (q > p) == desc;  // equal keys: swapping changes nothing
+        v[r] = swap ? q : p;
+        v[r | J] = swap ? p : q;
       }
     }
   }
+  if constexpr (J > 1) bitonic_step<K, E, S, J / 2>(v, lane);
+}
+
+template <typename K, int E, int S>
+__device__ __forceinline__ void bitonic_stage(K (&v)[E], int lane) {
+  bitonic_step<K, E, S, S / 2>(v, lane);
+  if constexpr (S < 64 * E) bitonic_stage<K, E, S * 2>(v, lane);
+}
+
+template <int E>
+__device__ __forceinline__ void bitonic_desc(uint64_t (&v)[E], int lane) {
+  bitonic_stage<uint64_t, E, 2>(v, lane);
 }
 
 // Sort the c (<= kCapMax) keys in buf descending; lanes then write the first k
@@ -217,34 +242,7 @@ __device__ __forceinline__ void sort_emit(uint64_t* buf, int c, int k, int lane,
 // The same network on 32-bit keys.
 template <int E>
 __device__ __forceinline__ void bitonic_desc32(uint32_t (&v)[E], int lane) {
-#pragma unroll
-  for (int s = 2; s <= 64 * E; s <<= 1) {
-#pragma unroll
-    for (int j = s >> 1; j > 0; j >>= 1) {
-      if (j >= E) {
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-          const uint32_t o = xor_shuffle(v[r], j / E, lane);
-          const int i = lane * E + r;
-          const bool lower = (i & j) == 0;
-          const bool desc = (i & s) == 0;
-          v[r] = ((o > v[r]) == (lower == desc)) ? o : v[r];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < E; r++) {
-          if ((r & j) == 0) {
-            const int i = lane * E + r;
-            const bool desc = (i & s) == 0;
-            const uint32_t p = v[r], q = v[r | j];
-            const bool swap = (q > p) == desc;
-            v[r] = swap ? q : p;
-            v[r | j] = swap ? p : q;
-          }
-        }
-      }
-    }
-  }
+  bitonic_stage<uint32_t, E, 2>(v, lane);
 }
 
 __device__ __forceinline__ int bitlen32(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
