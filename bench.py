@@ -452,8 +452,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "see DESIGN.md for how the path would shard across GPUs.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); streams (b,h) "
+              "are independent, so more GPUs would each run their share of them.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

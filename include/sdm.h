@@ -40,7 +40,7 @@ typedef enum {
   SDM_ERR_NULL = 1,        /* a required pointer is NULL */
   SDM_ERR_SHAPE = 2,       /* sizes inconsistent (odd d_k, W > N, N >= 2^31, ...) */
   SDM_ERR_DTYPE = 3,       /* unknown element type */
-  SDM_ERR_UNSUPPORTED = 4, /* valid problem outside this build's kernel limits */
+  SDM_ERR_UNSUPPORTED = 4, /* valid problem outside the kernels' limits */
   SDM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
   SDM_ERR_HIP = 6,         /* a HIP launch or runtime call failed */
   SDM_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */

@@ -404,7 +404,7 @@ const char* sdm_status_str(int s) {
     case SDM_ERR_NULL: return "null pointer";
     case SDM_ERR_SHAPE: return "inconsistent sizes";
     case SDM_ERR_DTYPE: return "unknown element type";
-    case SDM_ERR_UNSUPPORTED: return "outside this build's kernel limits";
+    case SDM_ERR_UNSUPPORTED: return "outside the kernels' limits";
     case SDM_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SDM_ERR_HIP: return "HIP launch failed";
     case SDM_ERR_WORKSPACE: return "workspace missing or too small";
