@@ -7,7 +7,12 @@
 // registers: 512 threads, each a 4-row x 8-column tile.  Per token, with
 // p = S k and r = S q taken from the old state:
 //   e = beta (v - alpha p),  o = alpha r + e (k . q),  S <- alpha S + e k^T
-// (o = S_t q expanded with S_t = alpha S + e k^T).  The two row reductions
+// (o = S_t q expanded with S_t = alpha S + e k^T).  The registers hold S as
+// A * Shat with a scalar A (the product of the alphas since the last fold), so
+// the decay costs one multiply per token instead of one per element:
+//   A' = alpha A,  Shat <- Shat + (e / A') k^T  (one FMA per element),
+// and A is folded back into Shat at every chunk of tokens (and at once when
+// alpha A falls below 2^-30, alpha = 0 included).  The two row reductions
 // over the 16 column tiles of a row run as one reduce-scatter butterfly; all
 // cross-lane moves stay inside 16-lane DPP rows (no LDS round trips).
 // Bound: fp32 VALU (4 d_v d_k FMA per token), not HBM.
@@ -102,6 +107,7 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
   }
   __syncthreads();
 
+  float A = 1.0f;  // S = A * s
   for (int tc0 = 0, cb = 0; tc0 < a.T; tc0 += kTC, cb ^= 1) {
     // prefetch the next chunk into registers
     const bool more = tc0 + kTC < a.T;
@@ -166,22 +172,42 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
       kq += xor_shuffle(kq, 4, lane);
       kq += xor_shuffle(kq, 8, lane);
       // lane holds row ri = 2b2+b1 of the tile: p if b3 == 0, r if b3 == 1
+      // (h1 is of the scaled state: the true p or r is A * h1)
       const int ri = 2 * b2 + b1;
       const float vrow = V[tt * kD + 4 * rg + ri];
-      const float e_own = beta * (vrow - alpha * h1);    // meaningful where b3 == 0
+      const float aA = alpha * A;                         // A' (uniform)
+      const float e_own = beta * (vrow - aA * h1);        // meaningful where b3 == 0
       const float e_row = xor_shuffle(e_own, 8, lane);   // e of the row, at b3 == 1
       if (b3 == 1 && b0 == 0 && tc0 + tt < a.T) {
-        const float o = fmaf(alpha, h1, e_row * kq);
+        const float o = fmaf(aA, h1, e_row * kq);
         a.out[((int64_t)st * a.T + tc0 + tt) * kD + 4 * rg + ri] = o;
       }
-      // e of the tile's 4 rows (held at lanes b3=0, 2b2+b1 = i)
-      const float e[4] = {row_bcast<0>(e_own), row_bcast<2>(e_own), row_bcast<4>(e_own),
-                          row_bcast<6>(e_own)};
+      float inv;
+      if (aA < 0x1p-30f) {  // fold now: s <- A' s, A <- 1 (alpha = 0 clears s)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 8; j++) s[i][j] *= aA;
+        A = 1.0f;
+        inv = 1.0f;
+      } else {
+        A = aA;
+        inv = __builtin_amdgcn_rcpf(aA);  // hardware reciprocal (1 ulp)
+      }
+      // e / A' of the tile's 4 rows (held at lanes b3=0, 2b2+b1 = i)
+      const float es = e_own * inv;
+      const float e[4] = {row_bcast<0>(es), row_bcast<2>(es), row_bcast<4>(es), row_bcast<6>(es)};
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) s[i][j] = fmaf(alpha, s[i][j], e[i] * kk[j]);
+        for (int j = 0; j < 8; j++) s[i][j] = fmaf(e[i], kk[j], s[i][j]);
     }
+    // fold A into s once per chunk
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) s[i][j] *= A;
+    A = 1.0f;
     if (more) {
       // everyone is done reading stage[cb ^ 1] (used two chunks ago)
 #pragma unroll
