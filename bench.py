@@ -433,6 +433,28 @@ def bench_raven(args, wl, dev):
     print(json.dumps(line), flush=True)
 
 
+def copy_bandwidth(gib=4.0, reps=5):
+    """Context for the scan's fraction of peak: read + write GB/s of a plain
+    device-to-device copy of `gib` GiB on this GPU (best of `reps`)."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * n * 4 / (best * 1e-3) / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -583,7 +605,9 @@ def main():
                 "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
         allb = stream_tokens * (scan_bytes_per_token(wl) + score_bytes_per_token(wl))
         kernels = {"score_topk_ms": round(ms_score, 4), "scan_ms": round(ms_scan, 4),
-                   "step_GBps_all_traffic": round(allb / (ms_step * 1e-3) / 1e9, 1)}
+                   "step_GBps_all_traffic": round(allb / (ms_step * 1e-3) / 1e9, 1),
+                   "model_tokens_per_s": round(wl.B * wl.T / (ms_wall * 1e-3), 1),
+                   "copy_GBps_measured": copy_bandwidth()}
 
     cpu = None
     if n_cpu:
