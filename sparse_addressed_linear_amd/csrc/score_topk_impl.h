@@ -376,7 +376,7 @@ template <int NT, int KS>
 __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok,
                                             const unsigned char* Pb, int n_tiles, int dh,
                                             int wave, int lane, float (&sc)[NT][4]) {
-  constexpr int TB = 8 / KS > 0 ? 8 / KS : 1;  // sub-key tiles loaded together
+  constexpr int TB = 16 / KS < NT ? 16 / KS : NT;  // sub-key tiles loaded together (16 loads)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int kq = lane >> 4;  // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
