@@ -648,9 +648,18 @@ struct ScoreZ {
   float w1, r1, w2, r2;
 };
 
-template <bool BF16, int NT, int NPL2>
+// TT: tokens per tile, 8 (every column used, each wave owns the key and query
+// columns of one token) or 4 for launches too small to fill the GPU (columns
+// of tokens 4..7 stay empty, and each wave owns one column: waves 0-3 the keys,
+// 4-7 the queries), which halves each wave's share of the serial per-column
+// work (sorts, stage 2) and so the latency of a tile.
+template <bool BF16, int NT, int NPL2, int TT>
 __global__ void __launch_bounds__(kThreads, 4)
     sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, ScoreZ z) {
+  static_assert(TT == kTT || TT == kTT / 2, "tile of 8 or 4 tokens");
+  constexpr int NCW = TT == kTT ? 2 : 1;  // columns each wave owns
+  // the o-th column owned by wave w
+  auto owned = [](int w, int o) { return TT == kTT ? w + o * kTT : (w & 3) + (w >> 2) * kTT; };
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float2 s_stat[kWaves][kCols];    // per wave: sum, sum of squares
   __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
@@ -677,10 +686,10 @@ __global__ void __launch_bounds__(kThreads, 4)
   grid_fill(a.W, rowoff, grid, wave, lane);
   if (L.gR) grid_fill(a.R, rowoff + (m + 1), grid + L.gW, wave, lane);
 
-  const int ntiles = (a.T + kTT - 1) / kTT;
+  const int ntiles = (a.T + TT - 1) / TT;
   const int tile_end = min(ntiles, (int)(blockIdx.x + 1) * tiles_per_wg);
   for (int tile = blockIdx.x * tiles_per_wg; tile < tile_end; tile++) {
-    const int t0 = tile * kTT;
+    const int t0 = tile * TT;
     for (int half = 0; half < 2; half++) {
       // Everything below is derived afresh from these in each half: values
       // kept live across halves would not fit in the register budget.
@@ -690,7 +699,7 @@ __global__ void __launch_bounds__(kThreads, 4)
       const int kq = hl >> 4;
       const bool is_q = tl >= kTT;
       const int tok = t0 + (tl & (kTT - 1));
-      const bool col_ok = tok < a.T;
+      const bool col_ok = (tl & (kTT - 1)) < TT && tok < a.T;
       const int kc = is_q ? a.R : a.W;
       const int capc = cap_for(kc);
       const float zc = is_q ? z.r1 : z.w1;
@@ -826,14 +835,14 @@ __global__ void __launch_bounds__(kThreads, 4)
         }
       }
       __syncthreads();
-      // one wave per column sorts: wave w owns the key and query columns of
-      // token t0 + w; the rank-ordered list of half h goes to [h*m, h*m + k)
-      // of the column's block (in place for h = 0: read before written)
-      if (t0 + hw < a.T) {
+      // one wave per column sorts (the columns `owned` by the wave); the
+      // rank-ordered list of half h goes to [h*m, h*m + k) of the column's
+      // block (in place for h = 0: read before written)
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-          const int cc = hw + q * kTT;
-          const int k = q ? a.R : a.W;
+      for (int o = 0; o < NCW; o++) {
+        const int cc = owned(hw, o);
+        if (t0 + (cc & (kTT - 1)) < a.T) {
+          const int k = cc >= kTT ? a.R : a.W;
           int c = 0;
 #pragma unroll
           for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
@@ -845,12 +854,13 @@ __global__ void __launch_bounds__(kThreads, 4)
       }
     }
 
-    // ---- 3. stage 2: this wave's two columns (lists written by this wave) ----
+    // ---- 3. stage 2: this wave's columns (lists written by this wave) ------
     wave_lds_sync();
-    const int tw = t0 + wave;
-    if (tw < a.T) {
-      for (int q = 0; q < 2; q++) {
-        const int cc = wave + q * kTT;
+    for (int o = 0; o < NCW; o++) {
+      const int cc = owned(wave, o);
+      const int tw = t0 + (cc & (kTT - 1));
+      const bool q = cc >= kTT;
+      if (tw < a.T) {
         const int k = q ? a.R : a.W;
         const bool own_grid = q && L.gR;
         uint64_t* blk = cand + cc * 2 * cm;
@@ -907,13 +917,18 @@ static inline float guess_z(int k, int n) {
 template <bool BF16, int NT, int NPL2>
 static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   const ScoreSmem L = score_smem(a.W, a.R);
-  auto k = sdm_score_topk_kernel<BF16, NT, NPL2>;
+  // tiles of 8 tokens unless they would leave CUs idle (decoding, short
+  // sequences): then tiles of 4, twice the workgroups, shorter per-tile chains
+  const bool small = (int64_t)((a.T + kTT - 1) / kTT) * a.S < kTargetWorkgroups;
+  auto k = small ? sdm_score_topk_kernel<BF16, NT, NPL2, kTT / 2>
+                 : sdm_score_topk_kernel<BF16, NT, NPL2, kTT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
   // token tiles per workgroup: up to 4 (one grid build serves them all)
   // while the launch still has at least 2048 workgroups
-  const int ntiles = (a.T + kTT - 1) / kTT;
+  const int tt = small ? kTT / 2 : kTT;
+  const int ntiles = (a.T + tt - 1) / tt;
   int per = 1;
   while (per < 4 && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
   dim3 grid((ntiles + per - 1) / per, a.S);
