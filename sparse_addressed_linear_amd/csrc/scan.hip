@@ -411,8 +411,10 @@ __global__ void __launch_bounds__(256) sdm_partial_sum_kernel(const float* __res
 
 template <int LPR, bool VBF16, int NW, int MC, int EPL>
 static hipError_t launch_scan_t(const ScanArgs& a, size_t lds, hipStream_t stream) {
-  auto k = a.tape ? sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, true>
-                  : sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, false>;
+  auto k = sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, false>;
+  if constexpr (NW > 1) {  // one-wave blocks are planned only without a tape
+    if (a.tape) k = sdm_scan_kernel<LPR, VBF16, NW, MC, EPL, true>;
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -420,11 +422,13 @@ static hipError_t launch_scan_t(const ScanArgs& a, size_t lds, hipStream_t strea
   return hipGetLastError();
 }
 
-ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R) {
+ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
   ScanPlan p{};
   p.lpr = (d_v % 32 == 0) ? 8 : 4;
   p.CS = d_v / (4 * p.lpr);
-  p.nw = 8;
+  // one token per stream (decoding): one-wave workgroups, so that several
+  // share a CU and the launch runs in one round instead of idling 7 waves each
+  p.nw = (T == 1 && !tape) ? 1 : 8;
   // partitions: enough workgroups to occupy every CU, while keeping enough
   // events per token and partition to fill a wave.
   int P = 1;
@@ -460,8 +464,12 @@ hipError_t launch_scan(const ScanArgs& a0, const ScanPlan& p, bool vbf16, hipStr
   const int mc = (a.W > a.R ? a.W : a.R) <= 64 ? 1 : ((a.W > a.R ? a.W : a.R) <= 128 ? 2 : 4);
 #define SDM_SCAN_CASE(LPR_, MC_, EPL_)                                           \
   if (p.lpr == LPR_ && mc == MC_ && p.epl == EPL_) {                             \
-    e = vbf16 ? launch_scan_t<LPR_, true, 8, MC_, EPL_>(a, p.lds, stream)        \
-              : launch_scan_t<LPR_, false, 8, MC_, EPL_>(a, p.lds, stream);      \
+    if (p.nw == 1)                                                               \
+      e = vbf16 ? launch_scan_t<LPR_, true, 1, MC_, EPL_>(a, p.lds, stream)      \
+                : launch_scan_t<LPR_, false, 1, MC_, EPL_>(a, p.lds, stream);    \
+    else                                                                         \
+      e = vbf16 ? launch_scan_t<LPR_, true, 8, MC_, EPL_>(a, p.lds, stream)      \
+                : launch_scan_t<LPR_, false, 8, MC_, EPL_>(a, p.lds, stream);    \
   } else
 #define SDM_SCAN_EPL(LPR_, MC_) \
   SDM_SCAN_CASE(LPR_, MC_, 8) SDM_SCAN_CASE(LPR_, MC_, 12) SDM_SCAN_CASE(LPR_, MC_, 16)

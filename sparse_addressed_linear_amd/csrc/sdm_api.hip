@@ -210,7 +210,8 @@ static int run_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_
   if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
   if (d->d_v % 16 != 0 || d->d_v > 512 || d->W > 256 || d->R > 256) return SDM_ERR_UNSUPPORTED;
   const int64_t N = (int64_t)d->n_sub * d->n_sub;
-  const sdm::ScanPlan p = sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
+  const sdm::ScanPlan p =
+      sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R, want_tape);
   if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
   if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
     return SDM_ERR_WORKSPACE;

@@ -188,7 +188,7 @@ struct ScanPlan {
   size_t work_bytes;
 };
 
-ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R);
+ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape = false);
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, bool vbf16, hipStream_t stream);
 
 struct ScoreArgs {
