@@ -367,8 +367,15 @@ def bench_raven(args, wl, dev):
     n_cpu = min(args.cpu_streams if args.cpu_streams is not None else 2, wl.streams)
     m0_cpu = [x["m0"][s // H, s % H].cpu() for s in range(n_cpu)]
     out = torch.empty((B, H, T, wl.d_v), device=dev)
-    need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
-    work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if args.timeparallel:
+        import ctypes
+        d = sdm.Dims(B, H, T, 2, wl.n_sub, wl.d_v, wl.W, wl.R)
+        need = int(sdm.lib().sdm_scan_timeparallel_workspace_size(ctypes.byref(d)))
+        scan_fn = sdm.scan_timeparallel
+    else:
+        need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
+        scan_fn = sdm.scan
+    work = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -377,7 +384,7 @@ def bench_raven(args, wl, dev):
         r = sdm.route_topk(x["zk"], x["zq"], x["a"], wl.W)
         if ev:
             ev[1].record(stream)
-        sdm.scan(x["m0"], *r, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
+        scan_fn(x["m0"], *r, x["v"], x["alpha"], x["beta"], out=out, workspace=work)
         if ev:
             ev[2].record(stream)
 
@@ -422,6 +429,9 @@ def bench_raven(args, wl, dev):
     cfg = {"workload": wl.name, "B": B, "H": H, "T": T, "M": wl.N, "K": wl.W, "d": wl.d_v,
            "content": "bf16" if wl.bf16 else "fp32", "table": "fp32",
            "table_GB": round(wl.table_bytes() / 1e9, 2)}
+    if args.timeparallel:
+        cfg["scan"] = "time-parallel"
+        roof["kernel"] = "sdm_scan_timeparallel (event keys, radix sort, slot segments, read sums)"
     line = {"metric": "Routed selective-decay slots: stream-tokens/sec (router + scan)",
             "value": round(st / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
