@@ -213,6 +213,8 @@ static int run_scan(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_
   const sdm::ScanPlan p =
       sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R, want_tape);
   if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  // one workgroup per (stream, column slice, partition): a 32-bit grid
+  if ((int64_t)d->B * d->H * p.CS * p.P > 0x7fffffffLL) return SDM_ERR_UNSUPPORTED;
   if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
     return SDM_ERR_WORKSPACE;
   if (!aligned16(M) || !aligned16(v) || !aligned16(out) ||
@@ -338,6 +340,8 @@ int sdm_scan_backward(const sdm_dims* d, sdm_dtype v_dtype, float* M, float* dM,
   const int64_t N = (int64_t)d->n_sub * d->n_sub;
   const sdm::ScanBwdPlan p = sdm::plan_scan_bwd(d->B * d->H, d->T, N, d->d_v, d->W, d->R);
   if (p.lds > kMaxLds) return SDM_ERR_UNSUPPORTED;
+  // one workgroup per (stream, partition): a 32-bit grid
+  if ((int64_t)d->B * d->H * p.P > 0x7fffffffLL) return SDM_ERR_UNSUPPORTED;
   if (p.work_bytes > 0 && (!workspace || workspace_bytes < p.work_bytes))
     return SDM_ERR_WORKSPACE;
   if (!aligned16(M) || !aligned16(dM) || !aligned16(v) || !aligned16(tape) || !aligned16(dout) ||
