@@ -295,6 +295,8 @@ def bench_train(args, wl, dev):
     out = torch.empty((B, H, T, wl.d_v), device=dev)
     need = sdm.scan_workspace_size(B, H, T, wl.N, wl.d_v, wl.W, wl.R)
     work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    sneed = sdm.score_topk_backward_workspace_size(B, H, T, wl.d_k, wl.n_sub, wl.W, wl.R)
+    swork = torch.empty(max(sneed, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -307,7 +309,7 @@ def bench_train(args, wl, dev):
         g = sdm.scan_backward(M, dM, *idx, x["v"], x["alpha"], x["beta"], tape, dout)
         rec(3)
         sdm.score_topk_backward(x["q"], x["k"], x["subkeys"], *idx, g["dwwt"], g["drwt"],
-                                dsubkeys=dC)
+                                dsubkeys=dC, workspace=swork)
         rec(4)
 
     for _ in range(args.warmup):

@@ -276,15 +276,27 @@ size_t sdm_scan_backward_workspace_size(const sdm_dims* dims);
  *   dsubkeys  [H][2][n_sub][d_k/2] fp32 in/out: the gradient is ADDED (the
  *                             caller clears it, or accumulates over calls)
  *
- * dq and dk are deterministic; dsubkeys is summed with float atomics, so its
- * last bits can differ between runs.  Kernel limits (else
- * SDM_ERR_UNSUPPORTED): n_sub <= 1024, d_k/2 <= 256, W, R <= 128.
+ *   workspace                 device scratch of at least
+ *                             sdm_score_topk_backward_workspace_size(dims)
+ *                             bytes, 256-byte aligned; contents not kept
+ *
+ * Every output is deterministic: each sum is taken in a fixed order.  The
+ * sub-key gradient is a sum per table row over the (token, side) pairs whose
+ * slots use that row; the library groups those contributions by row with a
+ * stable sort instead of accumulating them with atomics.  Kernel limits (else
+ * SDM_ERR_UNSUPPORTED): n_sub <= 1024, d_k/2 a multiple of 16 and <= 256,
+ * W, R <= 128, 4*B*H*T*max(W, R) < 2^31.  qp, kp, subkeys, dq, dk and
+ * dsubkeys must be 16-byte aligned (SDM_ERR_ALIGN).
  */
 int sdm_score_topk_backward(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp,
                             const void* kp, const void* subkeys, const int32_t* widx,
                             const float* wwt, const int32_t* ridx, const float* rwt,
                             const float* dwwt, const float* drwt, float* dq, float* dk,
-                            float* dsubkeys, void* stream);
+                            float* dsubkeys, void* workspace, size_t workspace_bytes,
+                            void* stream);
+/* Workspace bytes for sdm_score_topk_backward (0 when T == 0 or the problem
+ * is invalid). */
+size_t sdm_score_topk_backward_workspace_size(const sdm_dims* dims);
 
 /*
  * sdm_route_topk -- router of routed-slot writes with selective decay (Spanish

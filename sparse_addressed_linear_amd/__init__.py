@@ -26,6 +26,7 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE"
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
            "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
            "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
+           "sdm_score_topk_backward_workspace_size",
            "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
            "sdm_gdn_scan", "sdm_status_str", "sdm_version")
 
@@ -70,8 +71,10 @@ def lib():
         L.sdm_scan_backward.restype = ctypes.c_int
         L.sdm_scan_backward_workspace_size.argtypes = [PD]
         L.sdm_scan_backward_workspace_size.restype = SZ
-        L.sdm_score_topk_backward.argtypes = [PD, I32] + [P] * 13
+        L.sdm_score_topk_backward.argtypes = [PD, I32] + [P] * 13 + [SZ, P]
         L.sdm_score_topk_backward.restype = ctypes.c_int
+        L.sdm_score_topk_backward_workspace_size.argtypes = [PD]
+        L.sdm_score_topk_backward_workspace_size.restype = SZ
         L.sdm_scan_timeparallel.argtypes = [PD, I32] + [P] * 10 + [SZ, P]
         L.sdm_scan_timeparallel.restype = ctypes.c_int
         L.sdm_scan_timeparallel_workspace_size.argtypes = [PD]
@@ -194,6 +197,11 @@ def scan_workspace_size(B, H, T, N, d_v, W, R):
     return int(lib().sdm_scan_workspace_size(ctypes.byref(d)))
 
 
+def score_topk_backward_workspace_size(B, H, T, d_k, n_sub, W, R):
+    d = Dims(B, H, T, d_k, n_sub, 1, W, R)
+    return int(lib().sdm_score_topk_backward_workspace_size(ctypes.byref(d)))
+
+
 def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stream=None,
          tape=None):
     """Sparse gated-delta scan; M [B,H,N,d_v] fp32 is updated in place.
@@ -297,7 +305,7 @@ def scan_backward(M, dM, widx, wwt, ridx, rwt, v, alpha, beta, tape, dout, works
 
 
 def score_topk_backward(qp, kp, subkeys, widx, wwt, ridx, rwt, dwwt, drwt, dsubkeys=None,
-                        stream=None):
+                        workspace=None, stream=None):
     """Adjoint of the addressing.  Returns (dq, dk, dsubkeys), fp32; the
     sub-key gradient is added into ``dsubkeys`` when given (else a zeroed one)."""
     B, H, T, d_k = qp.shape
@@ -311,12 +319,16 @@ def score_topk_backward(qp, kp, subkeys, widx, wwt, ridx, rwt, dwwt, drwt, dsubk
         dsubkeys = torch.zeros(subkeys.shape, dtype=torch.float32, device=dev)
     d = Dims(B, H, T, d_k, n_sub, 1, W, R)
     f32 = torch.float32
+    need = int(lib().sdm_score_topk_backward_workspace_size(ctypes.byref(d)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     rc = lib().sdm_score_topk_backward(
         ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
         _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", f32), _dev(ridx, "ridx", torch.int32),
         _dev(rwt, "rwt", f32), _dev(dwwt, "dwwt", f32), _dev(drwt, "drwt", f32),
-        _dev(dq, "dq", f32), _dev(dk, "dk", f32), _dev(dsubkeys, "dsubkeys", f32),
-        _stream(stream))
+        _dev(dq, "dq", f32), _dev(dk, "dk", f32), _dev(dsubkeys, "dsubkeys", f32), wsp,
+        ctypes.c_size_t(need), _stream(stream))
     _check("sdm_score_topk_backward", rc)
     return dq, dk, dsubkeys
 

@@ -135,22 +135,44 @@ size_t sdm_scan_workspace_size(const sdm_dims* d) {
   return sdm::plan_scan(d->B * d->H, d->T, N, d->d_v, d->W, d->R).work_bytes;
 }
 
+// kernel limits of the addressing adjoint (record positions are 32-bit)
+static int score_bwd_shape_ok(const sdm_dims* d) {
+  const int dh = d->d_k / 2;
+  if (d->n_sub > 1024 || dh > 256 || dh % 16 != 0 || d->W > 128 || d->R > 128 ||
+      d->W > d->n_sub * d->n_sub || sdm::score_bwd_lds_bytes(d->W > d->R ? d->W : d->R) > kMaxLds ||
+      sdm::score_bwd_records(d->B * d->H, d->T, d->W, d->R) > 0x7fffffffLL)
+    return SDM_ERR_UNSUPPORTED;
+  return SDM_OK;
+}
+
+size_t sdm_score_topk_backward_workspace_size(const sdm_dims* d) {
+  if (!d || check_dims(d) != SDM_OK || score_bwd_shape_ok(d) != SDM_OK) return 0;
+  if (d->T == 0) return 0;
+  return sdm::score_bwd_workspace_bytes(d->B * d->H, d->T, d->H, d->n_sub, d->W, d->R);
+}
+
 int sdm_score_topk_backward(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
                             const void* kp, const void* subkeys, const int32_t* widx,
                             const float* wwt, const int32_t* ridx, const float* rwt,
                             const float* dwwt, const float* drwt, float* dq, float* dk,
-                            float* dsubkeys, void* stream) {
+                            float* dsubkeys, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   if (!d || !subkeys || !dsubkeys) return SDM_ERR_NULL;
   int rc = check_dims(d);
   if (rc) return rc;
   if (d->T > 0 && (!qp || !kp || !widx || !wwt || !ridx || !rwt || !dwwt || !drwt || !dq || !dk))
     return SDM_ERR_NULL;
   if (!valid_dtype(in_dtype)) return SDM_ERR_DTYPE;
-  const int dh = d->d_k / 2;
-  if (d->n_sub > 1024 || dh > 256 || d->W > 128 || d->R > 128 || d->W > d->n_sub * d->n_sub ||
-      sdm::score_bwd_lds_bytes(d->W > d->R ? d->W : d->R) > kMaxLds)
-    return SDM_ERR_UNSUPPORTED;
+  rc = score_bwd_shape_ok(d);
+  if (rc) return rc;
+  // rows of the inputs, of dq / dk and of the sub-key gradient move 16 bytes per lane
+  if (!aligned16(qp) || !aligned16(kp) || !aligned16(subkeys) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dsubkeys))
+    return SDM_ERR_ALIGN;
   if (d->T == 0) return SDM_OK;
+  const size_t need = sdm::score_bwd_workspace_bytes(d->B * d->H, d->T, d->H, d->n_sub, d->W, d->R);
+  if (!workspace || workspace_bytes < need) return SDM_ERR_WORKSPACE;
+  if (((uintptr_t)workspace) & 255) return SDM_ERR_ALIGN;
   sdm::ScoreBwdArgs a{};
   a.qp = qp;
   a.kp = kp;
@@ -171,7 +193,7 @@ int sdm_score_topk_backward(const sdm_dims* d, sdm_dtype in_dtype, const void* q
   a.n_sub = d->n_sub;
   a.W = d->W;
   a.R = d->R;
-  hipError_t e = sdm::launch_score_bwd(a, in_dtype == SDM_BF16, (hipStream_t)stream);
+  hipError_t e = sdm::launch_score_bwd(a, in_dtype == SDM_BF16, workspace, (hipStream_t)stream);
   return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
 }
 

@@ -131,12 +131,15 @@ struct ScoreBwdArgs {
   const float* drwt;       // [S][T][R]
   float* dq;               // [S][T][d_k]
   float* dk;
-  float* dsub;             // [H][2][n_sub][dh], accumulated
+  float* dsub;             // [H][2][n_sub][dh], accumulated (added to)
   int32_t S, H, T, d_k, n_sub, W, R;
 };
 
-hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, hipStream_t stream);
+// ws: score_bwd_workspace_bytes (records, their sorted copy, row bounds, sort scratch)
+hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStream_t stream);
 size_t score_bwd_lds_bytes(int kmax);  // kmax = max(W, R)
+int64_t score_bwd_records(int S, int T, int W, int R);
+size_t score_bwd_workspace_bytes(int S, int T, int H, int n_sub, int W, int R);
 
 // Reverse sweep of the scan (gradients).  Rows are whole (d_v = 4*LPR floats).
 struct ScanBwdArgs {

@@ -29,6 +29,7 @@ def test_header_declares_expected_entry_points():
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
          "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
          "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
+         "sdm_score_topk_backward_workspace_size",
          "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
          "sdm_gdn_scan", "sdm_status_str", "sdm_version"])
 
@@ -208,18 +209,32 @@ def test_gradient_entry_points_reject_before_any_launch(L):
     assert L.sdm_scan_backward(ctypes.byref(dims(T=0)), 0, P, P, *([z] * 14), z,
                                ctypes.c_size_t(0), None) == 0
 
-    # sdm_score_topk_backward: 12 pointers
-    def sbwd(d, null_at=None, dt=1):
+    # sdm_score_topk_backward: 12 pointers, then the workspace
+    sneed = L.sdm_score_topk_backward_workspace_size(ctypes.byref(d))
+    assert sneed > 0
+
+    def sbwd(d, null_at=None, dt=1, ptr_at=None, ws=None, wsp=P):
         args = [P] * 12
         if null_at is not None:
             args[null_at] = ctypes.c_void_p(0)
-        return L.sdm_score_topk_backward(ctypes.byref(d), dt, *args, None)
+        if ptr_at is not None:
+            args[ptr_at] = ctypes.c_void_p(4100)
+        return L.sdm_score_topk_backward(ctypes.byref(d), dt, *args, wsp,
+                                         ctypes.c_size_t(sneed if ws is None else ws), None)
     for i in range(12):
         assert sbwd(d, null_at=i) == 1, i
     assert sbwd(d, dt=2) == 3
     assert sbwd(dims(n_sub=2048, W=8)) == 4
     assert sbwd(dims(n_sub=256, W=129, R=8)) == 4
     assert sbwd(dims(d_k=31)) == 2
+    assert sbwd(dims(d_k=40)) == 4           # halves of 20: not a multiple of 16
+    for i in (0, 1, 2, 9, 10, 11):           # read or written 16 bytes a lane
+        assert sbwd(d, ptr_at=i) == 5, i
+    assert sbwd(d, ws=sneed - 1) == 7
+    assert sbwd(d, wsp=ctypes.c_void_p(0)) == 7
+    assert sbwd(d, wsp=ctypes.c_void_p(4096 + 16)) == 5   # the workspace is 256-byte aligned
+    assert L.sdm_score_topk_backward_workspace_size(ctypes.byref(dims(d_k=40))) == 0
+    assert L.sdm_score_topk_backward_workspace_size(ctypes.byref(dims(T=0))) == 0
 
 
 def test_route_topk_rejects_before_any_launch(L):

@@ -157,6 +157,27 @@ def test_score_backward_vs_oracle(dev):
         grad_close(np_(dC), ref["dsubkeys"], "dsubkeys")
 
 
+def test_score_backward_is_deterministic(dev):
+    """Every output of the addressing adjoint, the sub-key gradient included,
+    is the same bit for bit on repeated calls (each sum has a fixed order),
+    and a second call adds the same gradient again."""
+    wl = synth.WORKLOADS["mid"].with_(B=2, H=2, T=300)
+    say("case: score backward determinism", wl)
+    x = synth.make_inputs(wl, device=dev, with_m0=False)
+    g = sdm().score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    dw = torch.randn(g[1].shape, generator=gen, device=dev)
+    dr = torch.randn(g[3].shape, generator=gen, device=dev)
+    runs = [sdm().score_topk_backward(x["q"], x["k"], x["subkeys"], *g, dw, dr) for _ in range(3)]
+    acc = torch.zeros(x["subkeys"].shape, device=dev)
+    for _ in range(2):
+        sdm().score_topk_backward(x["q"], x["k"], x["subkeys"], *g, dw, dr, dsubkeys=acc)
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(runs[0], r))
+    assert torch.equal(acc, runs[0][2] + runs[0][2])
+
+
 def test_training_step_large_sampled(dev):
     """The large workload's forward with tape and both backward calls at full
     size (N = 2^20, 64 streams).  Two sampled streams run on the oracle's own
