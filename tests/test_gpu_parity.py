@@ -237,20 +237,51 @@ def check_scan(d, label):
     return M, out
 
 
+# Small tables (n_sub <= 32) and large ones with the same events: "hot"
+# confines the slots to [0, hot), so a large table can still have long
+# dependence chains inside a block of tokens, and W = R = 128 with hot slots
+# drives the overflow path.
 @pytest.mark.parametrize("label,args", [
     ("small d_v=16", dict(B=1, H=2, T=50, n_sub=16, d_v=16, W=8, R=8, seed=1)),
     ("d_v=64 partitions", dict(B=2, H=2, T=129, n_sub=64, d_v=64, W=32, R=32, seed=2)),
     ("bf16 v, ragged T", dict(B=1, H=3, T=77, n_sub=32, d_v=32, W=16, R=24, seed=3,
-                              v_bf16=True)),
-    ("hot slots, deep chains", dict(B=2, H=1, T=200, n_sub=32, d_v=32, W=16, R=16, seed=4,
+                                       v_bf16=True)),
+    ("hot slots, deep chains", dict(B=2, H=1, T=200, n_sub=64, d_v=32, W=16, R=16, seed=4,
                                     hot=48)),
-    ("hot slots W=1", dict(B=1, H=1, T=300, n_sub=8, d_v=32, W=1, R=3, seed=5, hot=4)),
-    ("overflow path", dict(B=4, H=4, T=40, n_sub=32, d_v=512, W=128, R=128, seed=6,
+    ("small table, hot slots", dict(B=2, H=1, T=200, n_sub=32, d_v=32, W=16, R=16, seed=4,
+                                hot=48)),
+    ("hot slots W=1", dict(B=1, H=1, T=300, n_sub=64, d_v=32, W=1, R=3, seed=5, hot=4)),
+    ("small table, W=1", dict(B=1, H=1, T=300, n_sub=8, d_v=32, W=1, R=3, seed=5, hot=4)),
+    ("overflow path", dict(B=4, H=4, T=40, n_sub=64, d_v=512, W=128, R=128, seed=6,
                            hot=300)),
-    ("T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
+    ("small table, d_v=512, W=R=128", dict(B=2, H=2, T=40, n_sub=32, d_v=512, W=128, R=128,
+                                       seed=6, hot=300)),
+    ("W=256, R=200", dict(B=1, H=2, T=20, n_sub=32, d_v=32, W=256, R=200, seed=8)),
+    ("T=1", dict(B=1, H=1, T=1, n_sub=64, d_v=32, W=4, R=4, seed=7)),
+    ("small table, T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
 ])
 def test_scan_vs_oracle(dev, label, args):
     check_scan(scan_case(dev, **args), label)
+
+
+def test_table_size_does_not_change_results(dev):
+    """The same events on a 1024-slot table and on a 4096-slot table whose
+    extra rows nothing touches (one slot partition at 160 streams either way):
+    the touched rows and the outputs are identical bit for bit, and the extra
+    rows keep their values."""
+    say("case: scan on a small and a large table")
+    small = scan_case(dev, B=10, H=16, T=40, n_sub=32, d_v=32, W=16, R=16, seed=12, hot=900)
+    big = dict(small)
+    M0b = torch.zeros((10, 16, 64 * 64, 32), device=dev)
+    M0b[:, :, :1024] = small["M0"]
+    big["M0"] = M0b
+    Ms, Mb = small["M0"].clone(), big["M0"].clone()
+    args = lambda d: (d["widx"], d["wwt"], d["ridx"], d["rwt"], d["v"], d["alpha"], d["beta"])
+    out_s = sdm().scan(Ms, *args(small))
+    out_b = sdm().scan(Mb, *args(big))
+    torch.cuda.synchronize()
+    assert torch.equal(Ms, Mb[:, :, :1024]) and torch.equal(out_s, out_b)
+    assert torch.equal(Mb[:, :, 1024:], M0b[:, :, 1024:])
 
 
 def test_scan_empty_sequence(dev):
