@@ -140,7 +140,8 @@ static int score_bwd_shape_ok(const sdm_dims* d) {
   const int dh = d->d_k / 2;
   if (d->n_sub > 1024 || dh > 256 || dh % 16 != 0 || d->W > 128 || d->R > 128 ||
       d->W > d->n_sub * d->n_sub || sdm::score_bwd_lds_bytes(d->W > d->R ? d->W : d->R) > kMaxLds ||
-      sdm::score_bwd_records(d->B * d->H, d->T, d->W, d->R) > 0x7fffffffLL)
+      sdm::score_bwd_records(d->B * d->H, d->T, d->W, d->R) > 0x7fffffffLL ||
+      (int64_t)d->H * 2 * d->n_sub >= 0x7fffffffLL)  // record keys (h, half, row) in 31 bits
     return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
