@@ -134,7 +134,9 @@ def test_score_backward_vs_oracle(dev):
     """Addressing adjoint on the oracle's own selections, bf16 and fp32 inputs."""
     for bf16, (B, H, T, d_k, n_sub, W, R) in ((True, (2, 3, 37, 128, 64, 32, 24)),
                                                (False, (1, 2, 20, 32, 32, 16, 8)),
-                                               (True, (1, 1, 9, 192, 128, 128, 100))):
+                                               (True, (1, 1, 9, 192, 128, 128, 100)),
+                                               # the largest shape the call takes
+                                               (True, (1, 1, 6, 512, 1024, 128, 128))):
         say(f"case: score backward bf16={bf16} B={B} H={H} T={T} d_k={d_k} n_sub={n_sub}")
         gen = torch.Generator().manual_seed(31 + T)
         q = torch.randn(B, H, T, d_k, generator=gen)

@@ -121,7 +121,12 @@ def test_score_topk_integer_ties(dev):
     for (B, H, T, d_k, n_sub, W, R) in ((1, 2, 40, 32, 64, 16, 12), (2, 1, 33, 64, 32, 32, 5),
                                         (1, 1, 17, 32, 128, 128, 128),
                                         # sub-key halves of 80 and 96: K padded to 128
-                                        (2, 1, 19, 160, 32, 32, 20), (1, 2, 29, 192, 128, 128, 97)):
+                                        (2, 1, 19, 160, 32, 32, 20), (1, 2, 29, 192, 128, 128, 97),
+                                        # largest shape the call takes: halves of 256, 1024
+                                        # sub-keys, W = R = 128
+                                        (1, 1, 9, 512, 1024, 128, 128),
+                                        # smallest table, every sub-key in the stage-1 lists
+                                        (1, 2, 11, 32, 16, 16, 16)):
         q = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         k = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         C = torch.randint(-1, 2, (H, 2, n_sub, d_k // 2), generator=g).float()
