@@ -372,11 +372,13 @@ namespace {
 // their scores are discarded by the caller).  There is no branch, and each
 // batch's loads are all in flight before its first MFMA.  xcol points at this
 // lane's column half (any valid row when !col_ok).
-template <int NT, int KS>
+template <int NT, int KS, int TBMAX>
 __device__ __forceinline__ void mfma_scores(const uint16_t* xcol, bool col_ok,
                                             const unsigned char* Pb, int n_tiles, int dh,
                                             int wave, int lane, float (&sc)[NT][4]) {
-  constexpr int TB = 16 / KS < NT ? 16 / KS : NT;  // sub-key tiles loaded together (16 loads)
+  // sub-key tiles loaded together (up to 16 loads, at most TBMAX tiles)
+  constexpr int TB0 = 16 / KS < NT ? 16 / KS : NT;
+  constexpr int TB = TB0 < TBMAX ? TB0 : TBMAX;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int kq = lane >> 4;  // which 8-wide K chunk of the 32
   bf16x8 bfrag[KS];
@@ -653,8 +655,21 @@ struct ScoreZ {
 // of tokens 4..7 stay empty, and each wave owns one column: waves 0-3 the keys,
 // 4-7 the queries), which halves each wave's share of the serial per-column
 // work (sorts, stage 2) and so the latency of a tile.
+// Waves per SIMD the kernel is compiled for.  With 8-token tiles and grids
+// of at most 5 keys a lane (k <= 71) a workgroup needs at most 46 KB of LDS
+// (40 KB at k = 64), so three fit on a CU if registers allow: the kernel is held to 80 VGPRs
+// (6 waves a SIMD; the stage-1 score codes then partly spill to scratch) and
+// loads its sub-key fragments two tiles at a time.  The extra workgroup covers
+// more of the dependent latency of the sorts and stage 2 than the spills cost.
+// Larger grids need more LDS (two workgroups a CU either way) and decoding
+// launches use too few workgroups for occupancy to matter: there 128 VGPRs.
+template <int NPL2, int TT>
+constexpr bool score_high_occ() {
+  return TT == kTT && NPL2 <= 5;
+}
+
 template <bool BF16, int NT, int NPL2, int TT>
-__global__ void __launch_bounds__(kThreads, 4)
+__global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4))
     sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, ScoreZ z) {
   static_assert(TT == kTT || TT == kTT / 2, "tile of 8 or 4 tokens");
   constexpr int NCW = TT == kTT ? 2 : 1;  // columns each wave owns
@@ -714,10 +729,11 @@ __global__ void __launch_bounds__(kThreads, 4)
         const int ksteps = score_ksteps(dh);
         const unsigned char* Pb = static_cast<const unsigned char*>(a.packed) +
                                   ((int64_t)h * 2 + half) * n_tiles * ksteps * 1024;
-        if (dh <= 32) mfma_scores<NT, 1>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
-        else if (dh <= 64) mfma_scores<NT, 2>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
-        else if (dh <= 128) mfma_scores<NT, 4>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
-        else mfma_scores<NT, 8>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        constexpr int TBM = score_high_occ<NPL2, TT>() ? 2 : 16;
+        if (dh <= 32) mfma_scores<NT, 1, TBM>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else if (dh <= 64) mfma_scores<NT, 2, TBM>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else if (dh <= 128) mfma_scores<NT, 4, TBM>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
+        else mfma_scores<NT, 8, TBM>(xcol, col_ok, Pb, n_tiles, dh, hw, hl, sc);
       } else {
         const float* xcol = static_cast<const float*>(is_q ? a.qp : a.kp) +
                             ((int64_t)st * a.T + (col_ok ? tok : 0)) * a.d_k + half * dh;
