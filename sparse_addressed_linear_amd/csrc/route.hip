@@ -10,16 +10,25 @@
 // sdm_scan.  Selection is on the logits (sigmoid is strictly increasing), with
 // ties to the lower slot index.
 //
-// One wave per (token, side).  The logits become order-preserving 32-bit keys
-// in LDS; a 4-digit radix select (8-bit digits, LDS histogram, suffix counts by
-// lane shuffles) finds the K-th largest key and how many keys equal to it are
-// taken (lowest indices first); the K winners are ranked by (key desc, index
-// asc) with one comparison sweep over the winner list, and written in rank
-// order with their gates.
+// One wave per (token, side), in one of two forms.
+//   * M <= 1024 slots: each lane holds the keys of slots lane, lane + 64, ...
+//     in registers as unique 64-bit keys (order-preserving logit bits, then the
+//     complemented slot).  A first threshold at the Gaussian quantile of the
+//     logits' mean and spread, then bisection on keys, leaves between K and
+//     cap_for(K) candidates.  They are compacted to LDS and sorted by a
+//     register bitonic network, and the first K are written in rank order with
+//     their gates.  The selection helpers are the addressing kernel's.
+//   * Larger M: the logits become order-preserving 32-bit keys in LDS.  A
+//     4-digit radix select (8-bit digits, LDS histogram, suffix counts by lane
+//     shuffles) finds the K-th largest key and how many keys equal to it are
+//     taken (lowest indices first).  The K winners are ranked by (key desc,
+//     index asc) with one comparison sweep over the winner list, and written
+//     in rank order with their gates.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "score_topk_impl.h"
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -154,9 +163,93 @@ __global__ void __launch_bounds__(kRouteWaves * 64) sdm_route_kernel(RouteArgs a
   }
 }
 
+// The K best of c sorted candidates in buf (descending keys), as slots and
+// gates in rank order: m = sigmoid(logit), r = m / (sum of the K kept m).
+template <int E>
+__device__ __forceinline__ void route_emit(const uint64_t* buf, int c, int K, int lane, int side,
+                                           float al, int32_t* oidx, float* oval) {
+  uint64_t v[E];
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int i = lane * E + r;
+    v[r] = i < c ? buf[i] : 0ull;
+  }
+  bitonic_desc<E>(v, lane);
+  float m[E];
+  float msum = 0.f;
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int p = lane * E + r;
+    m[r] = p < K ? 1.0f / (1.0f + expf(-key_score(v[r]))) : 0.f;
+    msum += m[r];
+  }
+  msum = wave_sum(msum);
+#pragma unroll
+  for (int r = 0; r < E; r++) {
+    const int p = lane * E + r;
+    if (p < K) {
+      const float rr = m[r] / msum;
+      oidx[p] = (int32_t)key_id(v[r]);
+      oval[p] = side ? rr : -expm1f(al * rr);
+    }
+  }
+}
+
+// Register form for M <= 64*KPL slots; zg: Gaussian quantile of the first
+// threshold (about 1.4K of the M logits above mean + zg * spread).
+template <int KPL>
+__global__ void __launch_bounds__(kRouteWaves * 64) sdm_route_reg_kernel(RouteArgs a, float zg) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int M = a.M, K = a.K;
+  uint64_t* buf = reinterpret_cast<uint64_t*>(smem) + (size_t)wave * kCapMax;
+  const int64_t unit = (int64_t)blockIdx.x * (kRouteWaves / 2) + (wave >> 1);
+  const int side = wave & 1;
+  if (unit >= a.units) return;  // wave-uniform; no barrier below
+  const float* z = (side ? a.zq : a.zk) + unit * M;
+
+  uint64_t key[KPL];
+  float sum = 0.f, sq = 0.f;
+  uint32_t mo = 0u;  // largest logit code
+#pragma unroll
+  for (int c = 0; c < KPL; c++) {
+    const int i = c * 64 + lane;
+    key[c] = 0ull;  // below every slot's key (whose low half is >= 1)
+    if (i < M) {
+      const float v = z[i];
+      key[c] = make_key(v, (uint32_t)i);
+      mo = max(mo, (uint32_t)(key[c] >> 32));
+      sum += v;
+      sq += v * v;
+    }
+  }
+  mo = wave_max32(mo);
+  sum = wave_sum(sum);
+  sq = wave_sum(sq);
+  const float mean = sum / M;
+  const float sd = sqrtf(fmaxf(sq / M - mean * mean, 0.f));
+  const uint64_t guess = (uint64_t)ord32(mean + zg * sd) << 32;
+  // K <= M slot keys are >= 1, so the threshold never admits the padding and
+  // leaves between K and cap_for(K) <= kCapMax keys
+  const uint64_t t =
+      find_threshold<KPL>(key, K, cap_for(K), guess, 0ull, ((uint64_t)mo + 1ull) << 32);
+  const int c = compact_ge<KPL>(key, t, buf, lane);
+  wave_lds_sync();
+  const float al = side ? 0.f : a.a[unit];
+  int32_t* oidx = (side ? a.ridx : a.widx) + unit * K;
+  float* oval = (side ? a.rwt : a.wcoef) + unit * K;
+  if (c <= 64) route_emit<1>(buf, c, K, lane, side, al, oidx, oval);
+  else if (c <= 128) route_emit<2>(buf, c, K, lane, side, al, oidx, oval);
+  else route_emit<4>(buf, c, K, lane, side, al, oidx, oval);
+}
+
+constexpr int kRouteRegMax = 1024;  // largest M of the register form
+
 }  // namespace
 
 size_t route_lds_bytes(int M, int K) {
+  if (M <= kRouteRegMax) return (size_t)kRouteWaves * kCapMax * sizeof(uint64_t);
   return (size_t)kRouteWaves * (M + 256 + 2 * K) * sizeof(uint32_t);
 }
 
@@ -164,6 +257,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (a.units == 0) return hipSuccess;
   const int64_t grid = (a.units + kRouteWaves / 2 - 1) / (kRouteWaves / 2);
   const size_t lds = route_lds_bytes(a.M, a.K);
+  if (a.M <= kRouteRegMax) {
+    const float zg = guess_z(a.K, a.M);
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kRouteWaves * 64), lds, stream, a, zg);
+      return hipGetLastError();
+    };
+    if (a.M <= 64) return launch(sdm_route_reg_kernel<1>);
+    if (a.M <= 128) return launch(sdm_route_reg_kernel<2>);
+    if (a.M <= 256) return launch(sdm_route_reg_kernel<4>);
+    if (a.M <= 512) return launch(sdm_route_reg_kernel<8>);
+    return launch(sdm_route_reg_kernel<16>);
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sdm_route_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -36,7 +36,9 @@ def sdm():
 def test_router_vs_oracle_with_ties(dev):
     g = torch.Generator().manual_seed(41)
     for (B, H, T, M, K) in ((1, 2, 33, 64, 8), (2, 1, 17, 1024, 32), (1, 1, 9, 4096, 128),
-                            (1, 1, 5, 100, 100)):
+                            (1, 1, 5, 100, 100),
+                            # register form: 256 candidates sorted at once, a ragged M, one slot
+                            (1, 2, 7, 1024, 128), (1, 1, 6, 1000, 77), (1, 1, 4, 1, 1)):
         say(f"case: router B={B} H={H} T={T} M={M} K={K}")
         # integer logits: many exact ties
         zk = torch.randint(-4, 5, (B, H, T, M), generator=g).float()
