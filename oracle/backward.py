@@ -165,7 +165,8 @@ def scan_backward_stream(M0, widx, wwt, ridx, rwt, v, alpha, beta, dout, dMT=Non
         # read of token t (it came after the write)
         r = ridx[t]
         drwt[t] = read_rows[t] @ dout[t]
-        dM[r] += rwt[t][:, None] * dout[t][None, :]
+        # a slot read more than once by one token takes every read's share
+        np.add.at(dM, r, rwt[t][:, None] * dout[t][None, :])
         # write of token t
         s = widx[t]
         G = dM[s].copy()

@@ -62,6 +62,28 @@ def test_scan_adjoint_equals_autograd(seed, hot):
         np.testing.assert_allclose(s[mine], a[ref], rtol=1e-11, atol=1e-11, err_msg=mine)
 
 
+def test_scan_adjoint_with_repeated_read_slots_equals_autograd():
+    """A token may read one slot more than once (the scan's contract asks only
+    write slots to be distinct): each read adds its own share of the output's
+    gradient to that row.  Weights are free inputs here (rows of a softmax)."""
+    c = stream_case(11, T=10, W=3, R=5, hot=7)
+    rng = np.random.default_rng(12)
+    # repeat slots inside reads: positions 1 and 3 copy position 0, and one
+    # token reads a single slot five times
+    c["ridx"][:, 1] = c["ridx"][:, 0]
+    c["ridx"][:, 3] = c["ridx"][:, 0]
+    c["ridx"][4, :] = c["ridx"][4, 2]
+    wwt = rng.dirichlet(np.ones(3), size=10)
+    rwt = rng.dirichlet(np.ones(5), size=10)
+    s = ob.scan_backward_stream(c["M0"], c["widx"], wwt, c["ridx"], rwt, c["v"], c["alpha"],
+                                c["beta"], c["dout"], c["dMT"])
+    a = ob.scan_grads_autograd(c["M0"], c["widx"], wwt, c["ridx"], rwt, c["v"], c["alpha"],
+                               c["beta"], c["dout"], c["dMT"])
+    for mine, ref in (("dM0", "M0"), ("dwwt", "wwt"), ("drwt", "rwt"), ("dv", "v"),
+                      ("dalpha", "alpha"), ("dbeta", "beta")):
+        np.testing.assert_allclose(s[mine], a[ref], rtol=1e-10, atol=1e-12, err_msg=mine)
+
+
 @pytest.mark.parametrize("seed,hot", [(4, None), (5, 8)])
 def test_composed_adjoints_equal_autograd_of_whole_path(seed, hot):
     c = stream_case(seed, hot=hot)
