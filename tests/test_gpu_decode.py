@@ -5,10 +5,10 @@ with T = 1, laid out head-major so that the tokens of one head score together.
 Rules:
   * stepping T tokens one call at a time gives the same bits as one call over
     the whole sequence: slot lists, weights, outputs and the final table;
-  * sampled streams match the oracle by the rules of the sequence tests: slot
-    sets modulo the gap rule, weights within 1e-5 + 1e-4|ref|, and end to end
-    (the oracle's own addressing and scan) table and outputs within
-    1e-5 + 1e-4|ref| for streams with no flagged token.
+  * streams match the oracle by the rules of the sequence tests: slot sets
+    modulo valid near-tie swaps, weights within 1e-5 + 1e-4|ref|, and end to
+    end (the oracle's own addressing and scan) table and outputs within
+    1e-5 + 1e-4|ref| outside the positions a valid swap taints.
 """
 import numpy as np
 import pytest
@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import close, compare_topk, np_, say
+from gpu_util import E2ETally, close, e2e_stream, np_, say
 
 pytestmark = pytest.mark.gpu
 
@@ -69,61 +69,52 @@ def test_decode_steps_equal_sequence_call(dev, use_packed):
         assert torch.equal(idx[j].permute(2, 1, 0, 3), g[j]), f"slot list {j} differs"
     assert torch.equal(outs.permute(2, 1, 0, 3), out_seq)
     assert torch.equal(M_dec.transpose(0, 1), M_seq)
-    # two sampled streams against the oracle's own addressing and scan, end to
-    # end from M0 (a stream holding a token flagged by the gap rule is skipped)
-    for b, h in ((0, 0), (wl.B - 1, wl.H - 1)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
-                                wl.W, wl.R)
-        flags = 0
-        for j, (ri, rw, gp) in enumerate(((ref["widx"], ref["wwt"], ref["wgap"]),
-                                           (ref["ridx"], ref["rwt"], ref["rgap"]))):
-            n, flagged, bad = compare_topk(np_(g[2 * j][sl]), np_(g[2 * j + 1][sl]), ri, rw, gp,
-                                           wl.N)
-            assert bad == 0
-            flags += flagged
-        M_ref = np.ascontiguousarray(M0_host[b:b + 1, h:h + 1])
-        o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
-                            np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
-        if flags:
-            say(f"  stream ({b},{h}) holds a flagged token; end to end not compared")
-            continue
-        assert np.all(close(np_(M_dec[h, b]), M_ref[0, 0]))
-        assert np.all(close(np_(outs[:, h, b]), o_ref[0, 0]))
+    # every stream against the oracle's own addressing and scan, end to end from M0
+    tot = E2ETally()
+    for b in range(wl.B):
+        for h in range(wl.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]),
+                                    np_(x["subkeys"][h:h + 1]), wl.W, wl.R)
+            M_ref = np.ascontiguousarray(M0_host[b:b + 1, h:h + 1])
+            o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
+                                np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
+            gl = [np_(idx[j][:, h, b]) for j in range(4)]
+            tot.add(e2e_stream(gl, ref, np_(x["k"][b, h]), np_(x["q"][b, h]),
+                               np_(x["subkeys"][h:h + 1]), np_(M_dec[h, b]), M_ref[0, 0],
+                               np_(outs[:, h, b]), o_ref[0, 0], msg=f"decode ({b},{h})"))
+    say(tot.line("decode vs oracle"))
+    assert tot.outs_compared >= 0.95 * tot.outs
 
 
 def test_decode_full_size_sampled(dev):
     """The serving batch at N = 2^20 (32 sequences x 8 heads, 68.7 GB table):
-    three steps, sampled streams checked against the oracle from M0."""
+    three steps; 16 streams spread over the batch and the heads checked end to
+    end against the oracle from M0 (each needs its 268 MB initial table on the
+    host)."""
     wl = synth.WORKLOADS["decode"].with_(T=3)
     say("case: decode full size, 3 steps", wl)
     x = synth.make_inputs(wl, device=dev, with_m0=False)
     xd = synth.decode_layout(x)
     M = synth.make_m0(wl, dev, head_major=True)
-    picks = ((0, 0), (17, 3), (wl.B - 1, wl.H - 1))
+    picks = tuple((2 * i + i // 8, i % wl.H) for i in range(15)) + ((wl.B - 1, wl.H - 1),)
     M0 = {p: np_(M[p[1], p[0]]) for p in picks}
     packed = sdm().pack_subkeys(x["subkeys"])
     idx, outs = run_decode(wl, xd, M, packed)
+    tot = E2ETally()
     for b, h in picks:
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
                                 wl.W, wl.R)
-        gi = [np_(idx[j][:, h, b])[None, None] for j in range(4)]
-        flags = 0
-        for j, (ri, rw, gp) in enumerate(((ref["widx"], ref["wwt"], ref["wgap"]),
-                                           (ref["ridx"], ref["rwt"], ref["rgap"]))):
-            n, flagged, bad = compare_topk(gi[2 * j], gi[2 * j + 1], ri, rw, gp, wl.N)
-            say(f"  stream ({b},{h}) {'WR'[j]}: {n} tokens, {flagged} flagged, {bad} mismatched")
-            assert bad == 0
-            flags += flagged
         # end to end against the oracle's own addressing and scan
         M_ref = np.ascontiguousarray(M0[(b, h)][None, None])
         o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
                             np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
-        if flags:
-            continue
-        assert np.all(close(np_(M[h, b]), M_ref[0, 0]))
-        assert np.all(close(np_(outs[:, h, b]), o_ref[0, 0]))
+        gl = [np_(idx[j][:, h, b]) for j in range(4)]
+        tot.add(e2e_stream(gl, ref, np_(x["k"][b, h]), np_(x["q"][b, h]),
+                           np_(x["subkeys"][h:h + 1]), np_(M[h, b]), M_ref[0, 0],
+                           np_(outs[:, h, b]), o_ref[0, 0], msg=f"decode ({b},{h})"))
+    say(tot.line("decode full size"))
     del M
     torch.cuda.empty_cache()
 
