@@ -245,6 +245,10 @@ int sdm_scan_record(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int
  *   drwt     [B][H][T][R]    fp32  out: dL/drwt
  *   workspace                       sdm_scan_backward_workspace_size(dims) bytes
  *
+ * Write slots must be distinct within a token (as for sdm_scan); read slots
+ * may repeat, and each read then adds its own share to the row's gradient (a
+ * block of 8 tokens holding such a token is swept one read at a time, which
+ * is slow but exact).
  * Results are deterministic.  The restored M equals M0 bit for bit (each
  * written row gets back its recorded value).  Kernel limits (else
  * SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256]; W, R <= 256.

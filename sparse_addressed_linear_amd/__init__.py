@@ -122,6 +122,29 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _want(t, shape, name, dtype=None):
+    """Check a caller-provided tensor's shape (and dtype) before a kernel
+    writes or reads it through a raw pointer."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _scratch(nbytes, device, stream=None, have=None):
+    """Device scratch of at least nbytes: `have` when big enough, else a new
+    uint8 tensor.  A tensor allocated here and used on a stream other than
+    the current one is recorded on that stream, so the caching allocator does
+    not hand its memory out again before the kernels that use it are done."""
+    if have is not None and have.numel() * have.element_size() >= nbytes:
+        return have
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 def _check(fn, rc):
     if rc != 0:
         raise SdmError(fn, rc)
@@ -139,8 +162,7 @@ def pack_subkeys(subkeys, workspace=None, stream=None):
     need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
     if need == 0:
         return None
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=subkeys.device)
+    workspace = _scratch(need, subkeys.device, stream, workspace)
     rc = lib().sdm_pack_subkeys(ctypes.byref(d), dt, _dev(subkeys, "subkeys"),
                                 _dev(workspace, "workspace"), ctypes.c_size_t(need),
                                 _stream(stream))
@@ -167,6 +189,10 @@ def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None, pac
                torch.empty((B, H, T, R), dtype=torch.int32, device=dev),
                torch.empty((B, H, T, R), dtype=torch.float32, device=dev))
     widx, wwt, ridx, rwt = out
+    _want(widx, (B, H, T, W), "widx")
+    _want(wwt, (B, H, T, W), "wwt")
+    _want(ridx, (B, H, T, R), "ridx")
+    _want(rwt, (B, H, T, R), "rwt")
     d = Dims(B, H, T, d_k, n_sub, 1, W, R)
     need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
     fn = "sdm_score_topk"
@@ -174,8 +200,8 @@ def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None, pac
         if packed.numel() * packed.element_size() < need:
             raise ValueError("packed sub-keys are smaller than these sizes need")
         workspace, fn = packed, "sdm_score_topk_packed"
-    elif need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif need:
+        workspace = _scratch(need, dev, stream, workspace)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     rc = getattr(lib(), fn)(ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"),
                             _dev(subkeys, "subkeys"), _dev(widx, "widx", torch.int32),
@@ -221,10 +247,11 @@ def scan(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspace=None, stre
     dt = _dtype_code(v)
     if out is None:
         out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
+    _want(out, (B, H, T, d_v), "out")
     d = Dims(B, H, T, 2, n_sub, d_v, W, R)
     need = int(lib().sdm_scan_workspace_size(ctypes.byref(d)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=M.device)
+    if need:
+        workspace = _scratch(need, M.device, stream, workspace)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     args = [_dev(M, "M", torch.float32), _dev(widx, "widx", torch.int32),
             _dev(wwt, "wwt", torch.float32), _dev(ridx, "ridx", torch.int32),
@@ -258,10 +285,10 @@ def scan_timeparallel(M, widx, wwt, ridx, rwt, v, alpha, beta, out=None, workspa
         raise ValueError("shape mismatch in scan_timeparallel arguments")
     if out is None:
         out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=M.device)
+    _want(out, (B, H, T, d_v), "out")
     d = Dims(B, H, T, 2, n_sub, d_v, W, R)
     need = int(lib().sdm_scan_timeparallel_workspace_size(ctypes.byref(d)))
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=M.device)
+    workspace = _scratch(max(need, 256), M.device, stream, workspace)
     f32 = torch.float32
     rc = lib().sdm_scan_timeparallel(
         ctypes.byref(d), _dtype_code(v), _dev(M, "M", f32), _dev(widx, "widx", torch.int32),
@@ -281,7 +308,10 @@ def scan_backward(M, dM, widx, wwt, ridx, rwt, v, alpha, beta, tape, dout, works
     n_sub = int(round(N ** 0.5))
     T, W = widx.shape[2], widx.shape[3]
     R = ridx.shape[3]
-    if dM.shape != M.shape or tape.shape != (B, H, T, W, d_v) or dout.shape != (B, H, T, d_v):
+    if dM.shape != M.shape or tape.shape != (B, H, T, W, d_v) or dout.shape != (B, H, T, d_v) \
+            or widx.shape[:2] != (B, H) or ridx.shape[:3] != (B, H, T) or wwt.shape != widx.shape \
+            or rwt.shape != ridx.shape or v.shape != (B, H, T, d_v) or alpha.shape != (B, H, T) \
+            or beta.shape != (B, H, T):
         raise ValueError("shape mismatch in scan_backward arguments")
     dev = M.device
     g = dict(dv=torch.empty((B, H, T, d_v), device=dev), dalpha=torch.empty((B, H, T), device=dev),
@@ -289,8 +319,8 @@ def scan_backward(M, dM, widx, wwt, ridx, rwt, v, alpha, beta, tape, dout, works
              drwt=torch.empty((B, H, T, R), device=dev))
     d = Dims(B, H, T, 2, n_sub, d_v, W, R)
     need = int(lib().sdm_scan_backward_workspace_size(ctypes.byref(d)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if need:
+        workspace = _scratch(need, dev, stream, workspace)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     f32 = torch.float32
     rc = lib().sdm_scan_backward(
@@ -309,19 +339,27 @@ def score_topk_backward(qp, kp, subkeys, widx, wwt, ridx, rwt, dwwt, drwt, dsubk
     """Adjoint of the addressing.  Returns (dq, dk, dsubkeys), fp32; the
     sub-key gradient is added into ``dsubkeys`` when given (else a zeroed one)."""
     B, H, T, d_k = qp.shape
+    if kp.shape != qp.shape or subkeys.dim() != 4 or subkeys.shape[0] != H or \
+            subkeys.shape[1] != 2 or subkeys.shape[3] * 2 != d_k:
+        raise ValueError("shape mismatch between qp, kp and subkeys")
     n_sub = subkeys.shape[2]
     W, R = widx.shape[3], ridx.shape[3]
+    for t, shape, name in ((widx, (B, H, T, W), "widx"), (wwt, (B, H, T, W), "wwt"),
+                           (dwwt, (B, H, T, W), "dwwt"), (ridx, (B, H, T, R), "ridx"),
+                           (rwt, (B, H, T, R), "rwt"), (drwt, (B, H, T, R), "drwt")):
+        _want(t, shape, name)
     dt = _dtype_code(qp, kp, subkeys)
     dev = qp.device
     dq = torch.empty((B, H, T, d_k), device=dev)
     dk = torch.empty((B, H, T, d_k), device=dev)
     if dsubkeys is None:
         dsubkeys = torch.zeros(subkeys.shape, dtype=torch.float32, device=dev)
+    _want(dsubkeys, subkeys.shape, "dsubkeys", torch.float32)
     d = Dims(B, H, T, d_k, n_sub, 1, W, R)
     f32 = torch.float32
     need = int(lib().sdm_score_topk_backward_workspace_size(ctypes.byref(d)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if need:
+        workspace = _scratch(need, dev, stream, workspace)
     wsp = _dev(workspace, "workspace") if need else ctypes.c_void_p(0)
     rc = lib().sdm_score_topk_backward(
         ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
@@ -403,6 +441,7 @@ def gdn_scan(S, k, q, v, alpha, beta, out=None, stream=None):
     dt = _dtype_code(k, q, v)
     if out is None:
         out = torch.empty((B, H, T, d_v), dtype=torch.float32, device=S.device)
+    _want(out, (B, H, T, d_v), "out")
     rc = lib().sdm_gdn_scan(B, H, T, d_k, d_v, dt, _dev(S, "S", torch.float32), _dev(k, "k"),
                             _dev(q, "q"), _dev(v, "v"), _dev(alpha, "alpha", torch.float32),
                             _dev(beta, "beta", torch.float32), _dev(out, "out", torch.float32),

@@ -30,6 +30,10 @@
 // event up front; level-L events reload theirs.  A token with more events in
 // its partition than a wave holds in registers sends its block down a serial
 // path (one wave at a time, in processing order, in register-sized chunks).
+// So does a token that reads one slot more than once (allowed: only write
+// slots must be distinct): its reads share a hash bit and would share a level,
+// so the serial path takes that block's reads one at a time, each adding its
+// own share to the row's gradient.
 //
 // Memory ordering is the forward kernel's: waves of a workgroup share the CU's
 // in-order vector L1, and a workgroup barrier orders earlier global stores
@@ -188,6 +192,9 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
     prefetch(b - 1);  // in flight while this block is processed
 
     // ---- 2. hash: slot -> events of the block (bit 2*wave + kind) ---------
+    // (a read whose bit is already set is a second read of that slot by the
+    // same token)
+    bool dupl = false;
     for (int e = lane; e < nev; e += 64) {
       const int32_t s = sl[e];
       const uint32_t bit = 1u << (2 * wave + ((ml[e] & kWrite) ? 1 : 0));
@@ -198,8 +205,9 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
                                        (unsigned long long)kEmpty, (unsigned long long)mine);
         if (old == kEmpty) break;
         if ((int32_t)(uint32_t)old == s) {
-          atomicOr(reinterpret_cast<unsigned long long*>(&htab[p]),
-                   (unsigned long long)((uint64_t)bit << 32));
+          const uint64_t prev = atomicOr(reinterpret_cast<unsigned long long*>(&htab[p]),
+                                         (unsigned long long)((uint64_t)bit << 32));
+          if ((prev >> 32) & bit) dupl = true;
           break;
         }
         p = (p + 1) & hmsk;
@@ -218,13 +226,16 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
     }
     wave_lds_sync();
     for (int o = 32; o > 0; o >>= 1) mylvl = max(mylvl, __shfl_xor(mylvl, o));
+    const bool wdup = __ballot(dupl) != 0ull;
     if (lane == 0) {
       if (mylvl > 0) atomicMax(&s_maxl, mylvl);
       if (nev > CAPW) atomicOr(&s_ovf, 1);
+      if (wdup) atomicOr(&s_ovf, 2);
     }
     __syncthreads();  // levels complete
     const int maxL = s_maxl;
     const bool ovf = s_ovf != 0;
+    const bool dup = (s_ovf & 2) != 0;
     for (int i = tid; i < a.hsize; i += NT) htab[i] = kEmpty;  // lookups are done
 
     float4 dvacc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -302,10 +313,22 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
       }
     } else {
       // ---- 4'. serial: one wave at a time in processing order; a wave's
-      // reads (distinct slots), then its writes (distinct slots) ------------
+      // reads, then its writes (distinct slots).  Reads go in register-sized
+      // chunks, or one at a time when a token of the block repeats a read
+      // slot (lane group 0 takes each; a read's stores reach the row before
+      // the next read's load) ----------------------------------------------
       for (int w = 0; w < kNW; w++) {
         if (wave == w) {
-          for (int part = 0; part < 2; part++) {
+          if (dup) {
+            for (int e = 0; e < nr; e++) {
+              const bool mine = g == 0;
+              const float4 X = load_x(e, mine);
+              const float4 D = load_d(e, mine);
+              apply(e, mine, X, D);
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            }
+          }
+          for (int part = dup ? 1 : 0; part < 2; part++) {
             const int lo = part ? nr : 0, hi = part ? nev : nr;
             for (int base = lo; base < hi; base += CAPW) {
               float4 X[EPL], D[EPL];

@@ -13,7 +13,11 @@
 // One wave per (token, side): side 0 is the write set (k', dk'), side 1 the
 // read set (q', dq').  The wave folds the dsigma of slots that share a sub-key
 // row in a small LDS hash per half (row -> dsigma sum and the row's first
-// event) and lists the distinct rows in the order of their first events.  It
+// event) and lists the distinct rows in the order of their first events.  The
+// fold adds 64-bit fixed-point integers (every dsigma of the wave scaled by
+// one power of two, so that 128 of them cannot overflow), so the order in
+// which the lanes' atomic adds land cannot change the sum: it is the exact sum
+// of the scaled values, rounded once back to fp32.  It
 // gathers those rows 16 bytes a lane for dx, and writes one record per
 // distinct row, (table row, token-side, dsigma sum), into fixed slots (unused
 // slots get only a key, one that sorts last; their payload is never read).
@@ -21,9 +25,9 @@
 // The table gradient is then a sum per table row over the records that name
 // it.  A radix sort (rocPRIM, stable) groups the records by row, keeping
 // their slot order inside a row, and one wave per table row adds
-// dsigma * x over its records in that order.  Every sum has a fixed order, so
-// dq', dk' and the sub-key gradient are the same bit for bit on every run,
-// and nothing is accumulated with atomics.
+// dsigma * x over its records in that order.  Every floating-point sum has a
+// fixed order and the fold's atomics add integers, so dq', dk' and the sub-key
+// gradient are the same bit for bit on every run.
 #include <hip/hip_runtime.h>
 #include <rocprim/device/device_radix_sort.hpp>
 #include <stdint.h>
@@ -53,18 +57,49 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // LDS hash of one half's rows for one wave: key row (-1 empty), the row's
-// first event (lowest rank) and its dsigma sum.
+// first event (lowest rank) and its dsigma sum in fixed point.
 struct RowEnt {
   int32_t key;
   int32_t first;
+  unsigned long long acc;  // two's complement sum of the scaled dsigma
+};
+
+// a distinct row of one half and its dsigma sum
+struct RowSum {
+  int32_t key;
   float sum;
 };
+
+// Fixed-point scale: with m = the wave's largest |dsigma| < 2^e, values are
+// multiplied by 2^(54 - e), so each is below 2^54 in magnitude and a sum of
+// at most 128 of them below 2^61.  The scaling is exact; rounding to an
+// integer drops only bits below 2^-54 of m.
+__device__ __forceinline__ int fixed_shift(float m) {
+  if (!(m > 0.f)) return 0;
+  int e;
+  frexpf(m, &e);
+  return 54 - e;
+}
+
+__device__ __forceinline__ unsigned long long to_fixed(float x, int sh) {
+  return (unsigned long long)(long long)rint(ldexp((double)x, sh));
+}
+
+__device__ __forceinline__ float from_fixed(unsigned long long a, int sh) {
+  return (float)ldexp((double)(long long)a, -sh);
+}
 
 // entries per half: a power of two >= 2k (k <= 128)
 __host__ __device__ inline int row_table_size(int k) {
   int n = 16;
   while (n < 2 * k) n *= 2;
   return n;
+}
+
+// LDS of one wave: two row tables and the distinct-row list (16-byte multiple)
+__host__ __device__ inline size_t wave_lds_bytes(int kmax) {
+  const size_t b = (size_t)2 * row_table_size(kmax) * sizeof(RowEnt) + (size_t)kmax * sizeof(RowSum);
+  return (b + 15) & ~(size_t)15;
 }
 
 template <bool BF16>
@@ -77,8 +112,8 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
   const int kmax = a.W > a.R ? a.W : a.R;
   const int HT = row_table_size(kmax);
   // per wave: two row tables, then the distinct rows of a half (row, sum)
-  RowEnt* tab = reinterpret_cast<RowEnt*>(smem) + (size_t)wave * (2 * HT + kmax);
-  RowEnt* dist = tab + 2 * HT;
+  RowEnt* tab = reinterpret_cast<RowEnt*>(smem + (size_t)wave * wave_lds_bytes(kmax));
+  RowSum* dist = reinterpret_cast<RowSum*>(tab + 2 * HT);
 
   const int64_t unit = (int64_t)blockIdx.x * (kWavesBwd / 2) + (wave >> 1);  // stream-token
   const int side = wave & 1;
@@ -108,11 +143,17 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
     rowv[1][u] = s - rowv[0][u] * n_sub;
   }
   const float dot = wave_sum(sw);
+  float mx = 0.f;
 #pragma unroll
-  for (int u = 0; u < 2; u++) ds[u] = wv[u] * (gv[u] - dot);
+  for (int u = 0; u < 2; u++) {
+    ds[u] = wv[u] * (gv[u] - dot);
+    mx = fmaxf(mx, fabsf(ds[u]));
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const int sh = fixed_shift(mx);
 
   // ---- fold events that share a row (per half) ----------------------------
-  for (int i = lane; i < 2 * HT; i += 64) tab[i] = RowEnt{-1, 0x7fffffff, 0.f};
+  for (int i = lane; i < 2 * HT; i += 64) tab[i] = RowEnt{-1, 0x7fffffff, 0ull};
   wave_lds_sync();
 #pragma unroll
   for (int u = 0; u < 2; u++) {
@@ -129,7 +170,7 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
           p = (p + 1) & (HT - 1);
         }
         atomicMin(&t[p].first, r);
-        atomicAdd(&t[p].sum, ds[u]);
+        atomicAdd(&t[p].acc, to_fixed(ds[u], sh));
       }
     }
   }
@@ -150,10 +191,10 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
         int p = (int)((uint32_t)rowv[half][u] * 2654435761u >> 8) & (HT - 1);
         while (t[p].key != rowv[half][u]) p = (p + 1) & (HT - 1);
         own = t[p].first == r;
-        sum = t[p].sum;
+        sum = from_fixed(t[p].acc, sh);
       }
       const uint64_t bal = __ballot(own);
-      if (own) dist[nd + __popcll(bal & below)] = RowEnt{rowv[half][u], 0, sum};
+      if (own) dist[nd + __popcll(bal & below)] = RowSum{rowv[half][u], sum};
       nd += __popcll(bal);
     }
     wave_lds_sync();
@@ -357,9 +398,7 @@ size_t bwd_sort_temp_bytes(int64_t n, int end_bit) {
 
 }  // namespace
 
-size_t score_bwd_lds_bytes(int kmax) {
-  return (size_t)kWavesBwd * (2 * row_table_size(kmax) + kmax) * sizeof(RowEnt);
-}
+size_t score_bwd_lds_bytes(int kmax) { return (size_t)kWavesBwd * wave_lds_bytes(kmax); }
 
 int64_t score_bwd_records(int S, int T, int W, int R) {
   return (int64_t)S * T * 4 * (W > R ? W : R);  // (token, side, half) x kmax

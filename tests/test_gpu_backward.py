@@ -47,13 +47,20 @@ def grad_close(g, r, what, rtol=2e-4):
                            f"worst |g-r| = {np.abs(g - r).max():.3e}, rms(ref) = {scale:.3e}")
 
 
-def scan_inputs(B, H, T, n_sub, d_v, W, R, seed, hot=None, v_bf16=False):
+def scan_inputs(B, H, T, n_sub, d_v, W, R, seed, hot=None, v_bf16=False, repeat_reads=False):
+    """Random scan inputs and gradients; `repeat_reads` makes tokens read
+    slots more than once (positions 1 and 3 repeat position 0, and every
+    fifth token reads one slot R times)."""
     g = torch.Generator().manual_seed(seed)
     N = n_sub * n_sub
     span = N if hot is None else hot
     n = B * H * T
     widx = torch.stack([torch.randperm(span, generator=g)[:W] for _ in range(n)])
     ridx = torch.stack([torch.randperm(span, generator=g)[:R] for _ in range(n)])
+    if repeat_reads:
+        ridx[:, 1] = ridx[:, 0]
+        ridx[:, 3] = ridx[:, 0]
+        ridx[::5] = ridx[::5, 2:3]
     d = dict(widx=widx.view(B, H, T, W).int(),
              wwt=torch.softmax(torch.randn(n, W, generator=g), -1).view(B, H, T, W),
              ridx=ridx.view(B, H, T, R).int(),
@@ -118,6 +125,10 @@ def check_stream(d, g, dM, b, h, label):
     ("hot W=1", dict(B=1, H=1, T=150, n_sub=8, d_v=32, W=1, R=3, seed=25, hot=4)),
     ("serial path", dict(B=2, H=2, T=30, n_sub=32, d_v=256, W=128, R=128, seed=26, hot=300)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=27)),
+    ("repeated read slots", dict(B=1, H=2, T=33, n_sub=16, d_v=32, W=8, R=8, seed=28, hot=40,
+                                 repeat_reads=True)),
+    ("repeated read slots, partitions", dict(B=2, H=2, T=41, n_sub=64, d_v=64, W=32, R=32,
+                                             seed=29, repeat_reads=True)),
 ])
 def test_scan_backward_vs_oracle(dev, label, args):
     say(f"case: scan backward {label}", args)
