@@ -60,50 +60,113 @@ def measured_scan_traffic(wl):
     return rec["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(wl, x, n_streams):
-    """Oracle (single thread) on the first n_streams streams, all tokens."""
+def host_threads():
+    """Host threads for the all-core oracle leg: the CPUs this process may use,
+    at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_stream(wl, host, m0, s):
+    """The oracle's addressing + scan of stream s from its initial table m0;
+    returns (addressing dict, seconds)."""
     import oracle
-    import synth
-    tok = 0
-    t_total = 0.0
-    for s in range(n_streams):
+    b, h = divmod(s, wl.H)
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    M = m0[None, None].copy()
+    t0 = time.perf_counter()
+    r = oracle.score_topk(host["q"][sl], host["k"][sl], host["subkeys"][h:h + 1], wl.W, wl.R)
+    oracle.scan(M, r["widx"], r["wwt"], r["ridx"], r["rwt"], host["v"][sl], host["alpha"][sl],
+                host["beta"][sl])
+    return r, time.perf_counter() - t0
+
+
+def cpu_baseline(wl, host, m0s, n_one, gpu_idx=None):
+    """The oracle timed on the host: single-threaded on the first n_one
+    streams, then all streams with one single-threaded oracle per stream on a
+    pool of host threads (the C oracle releases the GIL, so they run in
+    parallel).  With gpu_idx (the GPU's (widx, ridx) as host arrays) it also
+    counts the tokens whose slot sets differ from the oracle's."""
+    from concurrent.futures import ThreadPoolExecutor
+    t_one, tok_one = 0.0, 0
+    for s in range(n_one):
+        _, dt = _oracle_stream(wl, host, m0s[s], s)
+        t_one += dt
+        tok_one += wl.T
+    n = host_threads()
+    S = len(m0s)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        res = list(ex.map(lambda s: _oracle_stream(wl, host, m0s[s], s)[0], range(S)))
+    wall = time.perf_counter() - t0
+    out = {"value": S * wl.T / wall, "unit": "tokens/s", "cores": n, "kind": "oracle",
+           "sample": f"all {S} streams x {wl.T} tokens ({S * wl.T} stream-tokens), addressing + "
+                     f"scan, one single-threaded fp32 C oracle per stream on {n} host threads",
+           "one_core": {"value": tok_one / t_one if t_one else None, "unit": "tokens/s",
+                        "cores": 1,
+                        "sample": f"{n_one} of {S} streams x all {wl.T} tokens ({tok_one} "
+                                  "stream-tokens), single-threaded"}}
+    flags = None
+    if gpu_idx is not None:
+        flags = gap_flag_counts(wl, res, gpu_idx)
+    return out, flags
+
+
+def gap_flag_counts(wl, refs, gpu_idx, gap_tol=1e-5):
+    """Tokens whose GPU slot set differs from the oracle's: 'flagged' where the
+    oracle's relative gap between the k-th and (k+1)-th candidate is below
+    gap_tol (allowed), 'mismatched' otherwise (a failure)."""
+    import numpy as np
+    cnt = {"tokens_per_side": 0, "write_flagged": 0, "read_flagged": 0, "streams_flagged": 0,
+           "mismatched": 0, "streams": len(refs), "gap_tol": gap_tol}
+    for s, r in enumerate(refs):
         b, h = divmod(s, wl.H)
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        m0 = synth.to_numpy(x["m0_cpu"][s]) if "m0_cpu" in x else None
-        hq = synth.to_numpy(x["q"][sl])
-        hk = synth.to_numpy(x["k"][sl])
-        hc = synth.to_numpy(x["subkeys"][h:h + 1])
-        hv = synth.to_numpy(x["v"][sl])
-        ha = synth.to_numpy(x["alpha"][sl])
-        hb = synth.to_numpy(x["beta"][sl])
-        M = m0[None, None].copy()
-        t0 = time.perf_counter()
-        r = oracle.score_topk(hq, hk, hc, wl.W, wl.R)
-        oracle.scan(M, r["widx"], r["wwt"], r["ridx"], r["rwt"], hv, ha, hb)
-        t_total += time.perf_counter() - t0
-        tok += wl.T
-    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_streams} of {wl.streams} streams x all {wl.T} tokens "
-                      f"({tok} stream-tokens), addressing + scan, single-threaded fp32 C"}
+        any_flag = False
+        for side, key, gkey in (("write", "widx", "wgap"), ("read", "ridx", "rgap")):
+            g = np.sort(gpu_idx[key][b, h], -1)
+            o = np.sort(r[key][0, 0], -1)
+            diff = ~np.all(g == o, -1)
+            small = r[gkey][0, 0] < gap_tol
+            cnt[f"{side}_flagged"] += int((diff & small).sum())
+            cnt["mismatched"] += int((diff & ~small).sum())
+            any_flag |= bool((diff & small).any())
+        cnt["tokens_per_side"] += wl.T
+        cnt["streams_flagged"] += int(any_flag)
+    return cnt
 
 
-def cpu_baseline_gdn(wl, x, n_streams):
+def cpu_baseline_gdn(wl, x, n_one):
+    """The GDN oracle: single-threaded on n_one streams, then all streams on a
+    pool of host threads (one single-threaded oracle per stream)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     import synth
-    tok, t_total = 0, 0.0
-    for s in range(n_streams):
+    host = {n: synth.to_numpy(x[n]) for n in ("k", "q", "v", "alpha", "beta")}
+
+    def one(s):
         b, h = divmod(s, wl.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         S = np.zeros((1, 1, wl.d_v, wl.d_k), np.float32)
-        args = [synth.to_numpy(x[n][sl]) for n in ("k", "q", "v", "alpha", "beta")]
         t0 = time.perf_counter()
-        oracle.gdn_scan(S, *args)
-        t_total += time.perf_counter() - t0
-        tok += wl.T
-    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_streams} of {wl.streams} streams x all {wl.T} tokens "
-                      f"({tok} stream-tokens), single-threaded fp32 C"}
+        oracle.gdn_scan(S, *(host[n][sl] for n in ("k", "q", "v", "alpha", "beta")))
+        return time.perf_counter() - t0
+    t_one = sum(one(s) for s in range(n_one))
+    n = host_threads()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(one, range(wl.streams)))
+    wall = time.perf_counter() - t0
+    return {"value": wl.streams * wl.T / wall, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"all {wl.streams} streams x {wl.T} tokens, one single-threaded fp32 C "
+                      f"oracle per stream on {n} host threads",
+            "one_core": {"value": n_one * wl.T / t_one if t_one else None, "unit": "tokens/s",
+                         "cores": 1, "sample": f"{n_one} of {wl.streams} streams x all {wl.T} "
+                                               "tokens, single-threaded"}}
 
 
 def cpu_baseline_decode(wl, x, m0_cpu, n_streams):
@@ -529,13 +592,17 @@ def main():
           flush=True)
     x = synth.make_inputs(wl, device=dev)
     dense = wl.dense
-    # oracle sample sized for roughly 10-20 s of single-threaded CPU work
-    default_cpu = {"tiny": 1, "mid": 16, "large": 24, "long": 1, "gdn": 2}[wl.name]
+    # single-threaded oracle sample sized for roughly 10-20 s of CPU work; the
+    # all-core leg then runs every stream
+    default_cpu = {"tiny": 1, "mid": 16, "large": 24, "long": 1, "gdn": 16}[wl.name]
     n_cpu = args.cpu_streams if args.cpu_streams is not None else default_cpu
     n_cpu = min(n_cpu, wl.streams)
+    host, m0s = None, None
     if not dense and n_cpu:
-        # initial tables of the CPU sample, taken before the GPU steps modify M
-        x["m0_cpu"] = [x["m0"][s // wl.H, s % wl.H].cpu() for s in range(n_cpu)]
+        # host copies of every stream's inputs and initial table, taken before
+        # the GPU steps modify M
+        host = {n: synth.to_numpy(x[n]) for n in ("q", "k", "subkeys", "v", "alpha", "beta")}
+        m0s = [synth.to_numpy(x["m0"][s // wl.H, s % wl.H]) for s in range(wl.streams)]
 
     stream = torch.cuda.current_stream()
     if dense:
@@ -621,10 +688,15 @@ def main():
                    "model_tokens_per_s": round(wl.B * wl.T / (ms_wall * 1e-3), 1),
                    "copy_GBps_measured": copy_bandwidth()}
 
-    cpu = None
+    cpu, flags = None, None
     if n_cpu:
-        print(f"[bench] CPU baseline: oracle on {n_cpu} streams", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_gdn(wl, x, n_cpu) if dense else cpu_baseline(wl, x, n_cpu)
+        print(f"[bench] CPU baseline: oracle on {n_cpu} streams single-threaded, then all "
+              f"{wl.streams} streams on {host_threads()} threads", file=sys.stderr, flush=True)
+        if dense:
+            cpu = cpu_baseline_gdn(wl, x, n_cpu)
+        else:
+            gidx = {"widx": synth.to_numpy(idx_bufs[0]), "ridx": synth.to_numpy(idx_bufs[2])}
+            cpu, flags = cpu_baseline(wl, host, m0s, n_cpu, gidx)
 
     cfg = {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d_k": wl.d_k, "d_v": wl.d_v}
     if args.timeparallel:
@@ -638,6 +710,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "kernels": kernels, "ms_per_step_events": round(ms_step, 4)}
+    if flags is not None:
+        line["gap_flagged"] = flags
     print(json.dumps(line), flush=True)
 
 
