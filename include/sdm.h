@@ -43,7 +43,8 @@ typedef enum {
   SDM_ERR_UNSUPPORTED = 4, /* valid problem outside the kernels' limits */
   SDM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
   SDM_ERR_HIP = 6,         /* a HIP launch or runtime call failed */
-  SDM_ERR_WORKSPACE = 7    /* workspace missing or smaller than required */
+  SDM_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required */
+  SDM_ERR_SCRATCH = 8      /* needs more than the library's static scratch */
 } sdm_status;
 
 typedef enum {
@@ -94,6 +95,29 @@ typedef struct {
 int sdm_score_topk(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, const void* kp,
                    const void* subkeys, int32_t* widx, float* wwt, int32_t* ridx, float* rwt,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdm_score_topk_noalloc -- sdm_score_topk for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes no workspace.  The matrix-core copy of the
+ * sub-key tables that sdm_score_topk writes into the caller's workspace goes
+ * instead into a static device array of the library, 16 MiB per device, held
+ * from the library's load until the process ends.  Nothing is allocated or
+ * freed, on the device or the host.
+ *
+ * Arguments, layouts, results, limits and errors are sdm_score_topk's, plus:
+ * sizes whose sdm_score_topk_workspace_size exceeds 16 MiB return
+ * SDM_ERR_SCRATCH without enqueuing anything (bf16 needs 2 KiB per 16
+ * sub-keys per half per 32 elements of the half: up to 16 heads of 1024
+ * sub-keys with halves of 256; fp32 inputs need none).  The first call on a
+ * device looks up the array's address there (SDM_ERR_HIP if that fails).
+ * Every call on one device shares that device's array and rewrites it
+ * completely before reading it; two calls that overlap on one device (on
+ * different streams, or from several host threads) race on it.
+ */
+int sdm_score_topk_noalloc(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp,
+                           const void* kp, const void* subkeys, int32_t* widx, float* wwt,
+                           int32_t* ridx, float* rwt, void* stream);
 
 /* Bytes of device workspace sdm_score_topk needs for these sizes and input
  * type (0 when none, or when the sizes are invalid).  Pure host function.

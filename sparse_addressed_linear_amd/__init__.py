@@ -22,9 +22,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdm.so")
 SDM_F32, SDM_BF16 = 0, 1
 STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE",
           4: "SDM_ERR_UNSUPPORTED", 5: "SDM_ERR_ALIGN", 6: "SDM_ERR_HIP",
-          7: "SDM_ERR_WORKSPACE"}
+          7: "SDM_ERR_WORKSPACE", 8: "SDM_ERR_SCRATCH"}
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-           "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
+           "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_scan",
+           "sdm_scan_workspace_size", "sdm_scan_record",
            "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
            "sdm_score_topk_backward_workspace_size",
            "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
@@ -61,6 +62,8 @@ def lib():
         L.sdm_pack_subkeys.restype = ctypes.c_int
         L.sdm_score_topk_packed.argtypes = [PD, I32, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_score_topk_packed.restype = ctypes.c_int
+        L.sdm_score_topk_noalloc.argtypes = [PD, I32, P, P, P, P, P, P, P, P]
+        L.sdm_score_topk_noalloc.restype = ctypes.c_int
         L.sdm_score_topk_workspace_size.argtypes = [PD, I32]
         L.sdm_score_topk_workspace_size.restype = SZ
         L.sdm_scan.argtypes = [PD, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -209,6 +212,31 @@ def score_topk(qp, kp, subkeys, W, R, out=None, workspace=None, stream=None, pac
                             _dev(rwt, "rwt", torch.float32), wsp, ctypes.c_size_t(need),
                             _stream(stream))
     _check(fn, rc)
+    return widx, wwt, ridx, rwt
+
+
+def score_topk_noalloc(qp, kp, subkeys, W, R, out, stream=None):
+    """``score_topk`` through sdm_score_topk_noalloc: no workspace, no device
+    allocation (the library's static scratch holds the packed sub-keys).
+    ``out`` = (widx, wwt, ridx, rwt) must be given, so nothing is allocated
+    here either.  Overlapping calls on one device race on that scratch."""
+    B, H, T, d_k = qp.shape
+    if kp.shape != qp.shape or subkeys.dim() != 4 or subkeys.shape[0] != H or \
+            subkeys.shape[1] != 2 or subkeys.shape[3] * 2 != d_k:
+        raise ValueError("shape mismatch between qp, kp and subkeys")
+    n_sub = subkeys.shape[2]
+    dt = _dtype_code(qp, kp, subkeys)
+    widx, wwt, ridx, rwt = out
+    _want(widx, (B, H, T, W), "widx")
+    _want(wwt, (B, H, T, W), "wwt")
+    _want(ridx, (B, H, T, R), "ridx")
+    _want(rwt, (B, H, T, R), "rwt")
+    d = Dims(B, H, T, d_k, n_sub, 1, W, R)
+    rc = lib().sdm_score_topk_noalloc(
+        ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
+        _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", torch.float32),
+        _dev(ridx, "ridx", torch.int32), _dev(rwt, "rwt", torch.float32), _stream(stream))
+    _check("sdm_score_topk_noalloc", rc)
     return widx, wwt, ridx, rwt
 
 

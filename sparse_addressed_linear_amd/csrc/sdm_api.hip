@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sdm.h"
 #include "sdm_internal.h"
 
@@ -29,6 +31,33 @@ int check_dims(const sdm_dims* d) {
 }
 
 bool valid_dtype(int t) { return t == SDM_F32 || t == SDM_BF16; }
+
+// Scratch of sdm_score_topk_noalloc: the matrix-core copy of the sub-key
+// tables, in a file-scope device array instead of a caller's workspace.  Each
+// device holds its own copy at its own address; host code uses only the
+// address looked up per device below, never the array's name (which on the
+// host is a stand-in, not a device address).
+constexpr size_t kNoallocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SDM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SDM_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SDM_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SDM_OK;
+}
 
 }  // namespace
 
@@ -127,6 +156,23 @@ int sdm_score_topk_packed(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
                           void* stream) {
   return run_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt, workspace,
                    workspace_bytes, false, stream);
+}
+
+int sdm_score_topk_noalloc(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
+                           const void* kp, const void* subkeys, int32_t* widx, float* wwt,
+                           int32_t* ridx, float* rwt, void* stream) {
+  int rc = check_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt);
+  if (rc) return rc;
+  if (d->T == 0) return SDM_OK;
+  const size_t need =
+      sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
+  if (need > kNoallocScratchBytes) return SDM_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return run_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt, ws, need, true, stream);
 }
 
 size_t sdm_scan_workspace_size(const sdm_dims* d) {
@@ -436,6 +482,7 @@ const char* sdm_status_str(int s) {
     case SDM_ERR_ALIGN: return "pointer not 16-byte aligned";
     case SDM_ERR_HIP: return "HIP launch failed";
     case SDM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDM_ERR_SCRATCH: return "needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

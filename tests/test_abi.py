@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-         "sdm_score_topk_packed", "sdm_scan", "sdm_scan_workspace_size", "sdm_scan_record",
+         "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_scan",
+         "sdm_scan_workspace_size", "sdm_scan_record",
          "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
          "sdm_score_topk_backward_workspace_size",
          "sdm_route_topk", "sdm_scan_timeparallel", "sdm_scan_timeparallel_workspace_size",
@@ -41,8 +42,8 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert L.sdm_version().decode().count(".") == 2
-    for code in range(8):
-        assert L.sdm_status_str(code)
+    for code in range(9):
+        assert L.sdm_status_str(code) != b"unknown status"
     assert L.sdm_status_str(99) == b"unknown status"
 
 
@@ -271,3 +272,23 @@ def test_scan_timeparallel_rejects_before_any_launch(L):
     assert tp(d, wsp=ctypes.c_void_p(0)) == 7
     assert tp(d, wsp=ctypes.c_void_p(4112)) == 5   # not 256-byte aligned
     assert L.sdm_scan_timeparallel_workspace_size(ctypes.byref(dims(d_v=48))) == 0
+
+
+def test_score_topk_noalloc_rejects_on_the_host(L):
+    """Validation before any launch: bad arguments as sdm_score_topk's, and
+    sizes whose packed sub-key tables exceed the 16 MiB static scratch."""
+    noalloc = lambda d, dt=1, null_at=None: L.sdm_score_topk_noalloc(
+        ctypes.byref(d), dt, *[ctypes.c_void_p(0) if i == null_at else P for i in range(7)], None)
+    for i in range(7):
+        assert noalloc(dims(), null_at=i) == 1
+    assert noalloc(dims(d_k=31)) == 2
+    assert noalloc(dims(), dt=7) == 3
+    assert noalloc(dims(n_sub=2048, W=8)) == 4
+    # bf16: 2 KiB per 16 sub-keys per half per 32 elements of a half; 32 heads
+    # of 1024 sub-keys with halves of 256 need 32 MiB
+    assert noalloc(dims(H=32, d_k=512, n_sub=1024, W=64, R=64)) == 8
+    assert L.sdm_score_topk_workspace_size(ctypes.byref(dims(H=32, d_k=512, n_sub=1024, W=64,
+                                                              R=64)), 1) == 32 << 20
+    # 16 heads of that size fit exactly
+    assert L.sdm_score_topk_workspace_size(ctypes.byref(dims(H=16, d_k=512, n_sub=1024, W=64,
+                                                              R=64)), 1) == 16 << 20
