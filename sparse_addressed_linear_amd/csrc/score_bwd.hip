@@ -23,14 +23,21 @@
 // slots get only a key, one that sorts last; their payload is never read).
 //
 // The table gradient is then a sum per table row over the records that name
-// it.  A radix sort (rocPRIM, stable) groups the records by row, keeping
-// their slot order inside a row, and one wave per table row adds
-// dsigma * x over its records in that order.  Every floating-point sum has a
-// fixed order and the fold's atomics add integers, so dq', dk' and the sub-key
-// gradient are the same bit for bit on every run.
+// it.  A stable counting sort groups the records by row, keeping their
+// (token, side, half) order inside a row: the keys of one head are its 2*n_sub
+// sub-key rows, so each chunk of a stream's tokens counts them in an LDS
+// histogram; one exclusive scan over (row, chunk) gives every chunk's first
+// position per row; and one wave per chunk walks its groups in order, placing
+// each record at its row's next position.  The records of one group name
+// distinct rows, so that walk needs no atomics and its order is the input
+// order.  One wave per table row then adds dsigma * x over its records in
+// that order.  Every floating-point sum has a fixed order and the fold's
+// atomics add integers, so dq', dk' and the sub-key gradient are the same bit
+// for bit on every run.
 #include <hip/hip_runtime.h>
-#include <rocprim/device/device_radix_sort.hpp>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "sdm_internal.h"
 
@@ -39,8 +46,11 @@ namespace sdm {
 namespace {
 
 constexpr int kWavesBwd = 8;  // waves per workgroup (4 tokens x 2 sides)
-constexpr uint32_t kBwdPad = 0xffffffffu;  // key of an unused record slot (sorts last)
-constexpr int kRedWaves = 4;               // waves per workgroup of the row sums
+constexpr int kRedWaves = 4;  // waves per workgroup of the row sums
+constexpr int kChunks = 1024;  // counting-sort chunks a launch aims for
+constexpr int kStage = 1024;   // record slots of one scatter batch (256 threads x 4)
+constexpr int kScanPer = 16;  // elements per thread of the exclusive scan
+constexpr int kScanBlock = 256 * kScanPer;
 
 template <bool BF16>
 __device__ __forceinline__ float elem(const void* p, int64_t i) {
@@ -104,7 +114,8 @@ __host__ __device__ inline size_t wave_lds_bytes(int kmax) {
 
 template <bool BF16>
 __global__ void __launch_bounds__(kWavesBwd * 64)
-    sdm_score_bwd_kernel(ScoreBwdArgs a, uint32_t* __restrict__ rkey, uint64_t* __restrict__ rval) {
+    sdm_score_bwd_kernel(ScoreBwdArgs a, uint32_t* __restrict__ rkey, uint64_t* __restrict__ rval,
+                         int32_t* __restrict__ gcnt) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -219,16 +230,16 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
 #pragma unroll
     for (int e = 0; e < EL; e++) acc[e] = 0.f;
     {
-      // this half's records: distinct rows in the order of their first
-      // events, then padding keys up to kmax
+      // this half's records, group ts*2 + half: the distinct rows in the order
+      // of their first events, and how many there are
       const int64_t ts = unit * 2 + side;
       const int64_t r0 = (ts * 2 + half) * kmax;
       const uint32_t kbase = (uint32_t)((h * 2 + half) * n_sub);
-      for (int j = lane; j < kmax; j += 64) {
-        const bool on = j < nd;
-        rkey[r0 + j] = on ? kbase + (uint32_t)dist[j].key : kBwdPad;
-        if (on) rval[r0 + j] = ((uint64_t)ts << 32) | __float_as_uint(dist[j].sum);
+      for (int j = lane; j < nd; j += 64) {
+        rkey[r0 + j] = kbase + (uint32_t)dist[j].key;
+        rval[r0 + j] = ((uint64_t)ts << 32) | __float_as_uint(dist[j].sum);
       }
+      if (lane == 0) gcnt[ts * 2 + half] = nd;
     }
     for (int b0 = 0; b0 < nd; b0 += NI * RPI) {
       uint4 ch[NI];
@@ -269,23 +280,242 @@ __global__ void __launch_bounds__(kWavesBwd * 64)
   }
 }
 
-// Record boundaries: after the sort, rows [start, end) of the record list hold
-// table row key.  Rows no record names keep start = end = 0.
-__global__ void __launch_bounds__(256) sdm_bwd_bounds_clear(int32_t* bounds, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    bounds[i] = 0;
+// ---- stable counting sort of the records by table row ------------------------
+// Groups g = (token-side) * 2 + half hold gcnt[g] records at [g*kmax, ...), all
+// naming distinct rows of one head (keys h*2*n_sub .. +2*n_sub).  A chunk is
+// up to CH tokens of one stream (4 groups per token; CH is chosen so that a
+// launch has about kChunks chunks, each walked by one wave), and cnt holds, for
+// each head h, local key l and chunk c of that head (chunks of streams
+// b*H + h, ordered by b then position in the stream), the records of key l in
+// chunk c at cnt[(h*2*n_sub + l) * BnC + c]: its exclusive scan is the first
+// position of every (key, chunk) in the sorted list.
+struct SortGeom {
+  int T, H, n_sub, kmax, CH, nC, BnC;
+};
+
+// chunk (blockIdx.x, stream blockIdx.y): its head, its column in cnt, its groups
+__device__ __forceinline__ void chunk_of(const SortGeom& q, int& h, int& col, int64_t& g0,
+                                         int64_t& g1) {
+  const int st = blockIdx.y, tc = blockIdx.x;
+  h = st % q.H;
+  col = (st / q.H) * q.nC + tc;
+  const int64_t t0 = (int64_t)st * q.T + (int64_t)tc * q.CH;
+  const int64_t t1 = std::min((int64_t)st * q.T + q.T, t0 + q.CH);
+  g0 = t0 * 4;
+  g1 = t1 * 4;
 }
 
-__global__ void __launch_bounds__(256) sdm_bwd_bounds_kernel(const uint32_t* __restrict__ key,
-                                                             int64_t n, uint32_t nkeys,
-                                                             int32_t* __restrict__ bounds) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t k = key[i];
-    if (k >= nkeys) continue;  // padding (sorted after every real key)
-    if (i == 0 || key[i - 1] != k) bounds[2 * (int64_t)k] = (int32_t)i;
-    if (i == n - 1 || key[i + 1] != k) bounds[2 * (int64_t)k + 1] = (int32_t)(i + 1);
+__global__ void __launch_bounds__(256) sdm_bwd_count_kernel(SortGeom q,
+                                                            const uint32_t* __restrict__ rkey,
+                                                            const int32_t* __restrict__ gcnt,
+                                                            int32_t* __restrict__ cnt) {
+  extern __shared__ int32_t hist[];  // [2*n_sub]
+  int h, col;
+  int64_t g0, g1;
+  chunk_of(q, h, col, g0, g1);
+  const int nloc = 2 * q.n_sub;
+  const uint32_t kb = (uint32_t)h * nloc;
+  for (int l = threadIdx.x; l < nloc; l += 256) hist[l] = 0;
+  __syncthreads();
+  // record slots in batches of kU per thread: every group count of a batch
+  // is loaded before any key, and every key before any count is taken
+  constexpr int kU = 8;
+  const int64_t nslot = (g1 - g0) * q.kmax;
+  for (int64_t base = threadIdx.x; base < nslot; base += 256 * kU) {
+    int gc[kU];
+    uint32_t kk[kU];
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int64_t i = base + u * 256;
+      gc[u] = i < nslot ? gcnt[g0 + i / q.kmax] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int64_t i = base + u * 256;
+      const int64_t g = g0 + i / q.kmax;
+      const int j = (int)(i - (g - g0) * q.kmax);
+      kk[u] = (i < nslot && j < gc[u]) ? rkey[g * q.kmax + j] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; u++)
+      if (kk[u] != 0xffffffffu) atomicAdd(&hist[kk[u] - kb], 1);
+  }
+  __syncthreads();
+  for (int l = threadIdx.x; l < nloc; l += 256)
+    cnt[((int64_t)h * nloc + l) * q.BnC + col] = hist[l];
+}
+
+// Exclusive scan of n int32 in place (x[n] receives the total), in blocks of
+// kScanBlock: block sums, a scan of the block sums by one workgroup, then each
+// block's own scan plus its offset.
+__device__ __forceinline__ int block_excl_scan256(int v, int* tmp) {
+  // exclusive prefix of v over the 256 threads of the block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; i++) before += tmp[i];
+  __syncthreads();
+  return before + inc - v;
+}
+
+__global__ void __launch_bounds__(256) sdm_scan_sums_kernel(const int32_t* __restrict__ x,
+                                                            int64_t n, int32_t* __restrict__ bsum) {
+  __shared__ int tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanPer;
+  int s = 0;
+  for (int i = 0; i < kScanPer; i++) s += base + i < n ? x[base + i] : 0;
+  const int ex = block_excl_scan256(s, tmp);
+  if (threadIdx.x == 255) bsum[blockIdx.x] = ex + s;
+}
+
+__global__ void __launch_bounds__(256) sdm_scan_top_kernel(int32_t* __restrict__ bsum, int nb,
+                                                           int32_t* __restrict__ total) {
+  __shared__ int tmp[4];
+  const int per = (nb + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  int s = 0;
+  for (int i = 0; i < per; i++) s += b0 + i < nb ? bsum[b0 + i] : 0;
+  int run = block_excl_scan256(s, tmp);
+  for (int i = 0; i < per; i++) {
+    if (b0 + i < nb) {
+      const int v = bsum[b0 + i];
+      bsum[b0 + i] = run;
+      run += v;
+    }
+  }
+  if (threadIdx.x == 255) *total = run;
+}
+
+__global__ void __launch_bounds__(256) sdm_scan_down_kernel(int32_t* __restrict__ x, int64_t n,
+                                                            const int32_t* __restrict__ bsum) {
+  __shared__ int tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanPer;
+  int v[kScanPer];
+  int s = 0;
+  for (int i = 0; i < kScanPer; i++) {
+    v[i] = base + i < n ? x[base + i] : 0;
+    s += v[i];
+  }
+  int run = block_excl_scan256(s, tmp) + bsum[blockIdx.x];
+  for (int i = 0; i < kScanPer; i++) {
+    if (base + i < n) x[base + i] = run;
+    run += v[i];
+  }
+}
+
+// Scatter: the chunk's groups go in batches of up to 32, in order.  In a
+// batch, every record sets its group's bit in an LDS mask of its row (the
+// records of one group name distinct rows, and OR does not depend on the
+// order it is applied in); a record's position is then its row's next
+// position plus the number of earlier groups of the batch that name the row;
+// and the record of the row's last group in the batch advances that next
+// position past the batch.  So every record lands where a walk in group
+// order would put it, with no serial step.  The next batch's records are
+// loaded while a batch is placed, and its group counts one batch earlier.
+__global__ void __launch_bounds__(256) sdm_bwd_scatter_kernel(
+    SortGeom q, const uint32_t* __restrict__ rkey, const uint64_t* __restrict__ rval,
+    const int32_t* __restrict__ gcnt, const int32_t* __restrict__ offs,
+    uint64_t* __restrict__ vout) {
+  extern __shared__ int32_t lds[];
+  const int nloc = 2 * q.n_sub;
+  int32_t* run = lds;                                     // [nloc] next position of each row
+  uint32_t* mask = reinterpret_cast<uint32_t*>(lds + nloc);  // [nloc] groups of the batch
+  int h, col;
+  int64_t g0, g1;
+  chunk_of(q, h, col, g0, g1);
+  const uint32_t kb = (uint32_t)h * nloc;
+  const int tid = threadIdx.x;
+  {
+    // every first position is loaded before any is stored (one round trip)
+    constexpr int kU = 8;
+    for (int l0 = tid; l0 < nloc; l0 += 256 * kU) {
+      int v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; u++) {
+        const int l = l0 + u * 256;
+        v[u] = l < nloc ? offs[((int64_t)h * nloc + l) * q.BnC + col] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; u++)
+        if (l0 + u * 256 < nloc) {
+          run[l0 + u * 256] = v[u];
+          mask[l0 + u * 256] = 0u;
+        }
+    }
+  }
+  const int sg = std::max(1, std::min(32, kStage / q.kmax));  // groups per batch
+  constexpr int kU = kStage / 256;  // record slots per thread per batch
+  // slot i = tid + u*256 of a batch is record j = i % kmax of group i / kmax
+  auto counts = [&](int64_t gs, int (&gc)[kU]) {
+    const int nrec = (int)std::min<int64_t>(sg, g1 - gs) * q.kmax;
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int i = tid + u * 256;
+      gc[u] = (gs < g1 && i < nrec) ? gcnt[gs + i / q.kmax] : 0;
+    }
+  };
+  auto records = [&](int64_t gs, const int (&gc)[kU], uint32_t (&kk)[kU], uint64_t (&vv)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      const int i = tid + u * 256;
+      const int gq = i / q.kmax, j = i - gq * q.kmax;
+      const bool on = j < gc[u];  // gc is 0 past the batch
+      kk[u] = on ? rkey[(gs + gq) * q.kmax + j] : 0xffffffffu;
+      vv[u] = on ? rval[(gs + gq) * q.kmax + j] : 0ull;
+    }
+  };
+  int gcn[kU], gcnn[kU];
+  uint32_t kn[kU];
+  uint64_t vn[kU];
+  counts(g0, gcn);
+  records(g0, gcn, kn, vn);
+  counts(g0 + sg, gcnn);
+  __syncthreads();  // run and mask are filled
+  for (int64_t gs = g0; gs < g1; gs += sg) {
+    uint32_t kc[kU];
+    uint64_t vc[kU];
+#pragma unroll
+    for (int u = 0; u < kU; u++) kc[u] = kn[u], vc[u] = vn[u];
+    // the next batch in flight
+    records(gs + sg, gcnn, kn, vn);
+    counts(gs + 2 * sg, gcnn);
+    // 1. groups naming each row
+#pragma unroll
+    for (int u = 0; u < kU; u++)
+      if (kc[u] != 0xffffffffu) atomicOr(&mask[kc[u] - kb], 1u << ((tid + u * 256) / q.kmax));
+    __syncthreads();
+    // 2. positions
+    uint32_t m[kU];
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      m[u] = 0u;
+      if (kc[u] != 0xffffffffu) {
+        const int loc = (int)(kc[u] - kb);
+        const int gq = (tid + u * 256) / q.kmax;
+        m[u] = mask[loc];
+        vout[run[loc] + __popc(m[u] & ((1u << gq) - 1u))] = vc[u];
+      }
+    }
+    __syncthreads();
+    // 3. the row's last group of the batch moves its next position on
+#pragma unroll
+    for (int u = 0; u < kU; u++) {
+      if (kc[u] != 0xffffffffu) {
+        const int gq = (tid + u * 256) / q.kmax;
+        if ((m[u] >> gq) == 1u) {
+          const int loc = (int)(kc[u] - kb);
+          run[loc] += __popc(m[u]);
+          mask[loc] = 0u;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -299,14 +529,14 @@ __global__ void __launch_bounds__(256) sdm_bwd_bounds_kernel(const uint32_t* __r
 template <bool BF16>
 __global__ void __launch_bounds__(kRedWaves * 64)
     sdm_score_bwd_reduce_kernel(ScoreBwdArgs a, const uint64_t* __restrict__ rval,
-                                const int32_t* __restrict__ bounds) {
+                                const int32_t* __restrict__ offs, int BnC) {
   constexpr int EL = BF16 ? 8 : 4;  // elements per 16-byte chunk
   constexpr int NI = 4;
   const int lane = threadIdx.x & 63;
   const int64_t key = (int64_t)blockIdx.x * kRedWaves + (threadIdx.x >> 6);
   const int64_t nkeys = (int64_t)a.H * 2 * a.n_sub;
   if (key >= nkeys) return;  // wave-uniform; no barrier follows
-  const int i0 = bounds[2 * key], i1 = bounds[2 * key + 1];
+  const int i0 = offs[key * BnC], i1 = offs[(key + 1) * BnC];
   if (i1 <= i0) return;
   const int dh = a.d_k / 2;
   const int half = (int)((key / a.n_sub) & 1);
@@ -378,23 +608,22 @@ __global__ void __launch_bounds__(kRedWaves * 64)
   }
 }
 
-int bits_for(int64_t n) {  // bits to hold 0 .. n-1
-  int b = 0;
-  while ((int64_t{1} << b) < n) b++;
-  return b;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
 
-// rocPRIM's scratch for n pairs (a query; nothing runs)
-size_t bwd_sort_temp_bytes(int64_t n, int end_bit) {
-  size_t bytes = 0;
-  const hipError_t e =
-      rocprim::radix_sort_pairs(nullptr, bytes, (const uint32_t*)nullptr, (uint32_t*)nullptr,
-                                (const uint64_t*)nullptr, (uint64_t*)nullptr, (size_t)n, 0,
-                                (unsigned)end_bit);
-  return e == hipSuccess ? bytes : SIZE_MAX / 4;  // an unmet size rather than a wrong one
+SortGeom sort_geom(int S, int T, int H, int n_sub, int W, int R) {
+  SortGeom q;
+  q.T = T;
+  q.H = H;
+  q.n_sub = n_sub;
+  q.kmax = W > R ? W : R;
+  const int64_t per = ((int64_t)S * T + kChunks - 1) / kChunks;
+  q.CH = (int)std::min<int64_t>(std::max<int64_t>(per, 32), 1024);
+  q.nC = (T + q.CH - 1) / q.CH;
+  q.BnC = (S / H) * q.nC;
+  return q;
 }
+
+size_t scatter_lds_bytes(const SortGeom& q) { return (size_t)2 * (2 * q.n_sub) * 4; }
 
 }  // namespace
 
@@ -404,33 +633,38 @@ int64_t score_bwd_records(int S, int T, int W, int R) {
   return (int64_t)S * T * 4 * (W > R ? W : R);  // (token, side, half) x kmax
 }
 
+// records (keys, payloads, sorted payloads), group counts, the (row, chunk)
+// counts and their scan, and the scan's block sums
 size_t score_bwd_workspace_bytes(int S, int T, int H, int n_sub, int W, int R) {
   const int64_t n = score_bwd_records(S, T, W, R);
-  const int64_t nkeys = (int64_t)H * 2 * n_sub;
-  const int end_bit = bits_for(nkeys + 1);
-  return 2 * align256((size_t)n * 4) + 2 * align256((size_t)n * 8) +
-         align256((size_t)nkeys * 8) + align256(bwd_sort_temp_bytes(n, end_bit));
+  const SortGeom q = sort_geom(S, T, H, n_sub, W, R);
+  const int64_t M = (int64_t)H * 2 * n_sub * q.BnC;
+  const int64_t nb = (M + kScanBlock - 1) / kScanBlock;
+  return align256((size_t)n * 4) + 2 * align256((size_t)n * 8) +
+         align256((size_t)S * T * 4 * 4) + align256((size_t)(M + 1) * 4) +
+         align256((size_t)nb * 4);
 }
 
 hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStream_t stream) {
   const int64_t units = (int64_t)a.S * a.T;
   if (units == 0) return hipSuccess;
   const int64_t n = score_bwd_records(a.S, a.T, a.W, a.R);
+  const SortGeom q = sort_geom(a.S, a.T, a.H, a.n_sub, a.W, a.R);
   const int64_t nkeys = (int64_t)a.H * 2 * a.n_sub;
-  const int end_bit = bits_for(nkeys + 1);
+  const int64_t M = nkeys * q.BnC;
+  const int64_t nb = (M + kScanBlock - 1) / kScanBlock;
   unsigned char* p = static_cast<unsigned char*>(ws);
-  uint32_t* k_in = reinterpret_cast<uint32_t*>(p);
+  uint32_t* rkey = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)n * 4);
-  uint32_t* k_out = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)n * 4);
-  uint64_t* v_in = reinterpret_cast<uint64_t*>(p);
+  uint64_t* rval = reinterpret_cast<uint64_t*>(p);
   p += align256((size_t)n * 8);
-  uint64_t* v_out = reinterpret_cast<uint64_t*>(p);
+  uint64_t* vout = reinterpret_cast<uint64_t*>(p);
   p += align256((size_t)n * 8);
-  int32_t* bounds = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)nkeys * 8);
-  size_t tmp_bytes = bwd_sort_temp_bytes(n, end_bit);
-  void* tmp = p;
+  int32_t* gcnt = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)units * 4 * 4);
+  int32_t* offs = reinterpret_cast<int32_t*>(p);  // counts, then their exclusive scan
+  p += align256((size_t)(M + 1) * 4);
+  int32_t* bsum = reinterpret_cast<int32_t*>(p);
 
   // 1. per (token, side): dsigma, dx, one record per distinct table row
   const int64_t grid = (units + kWavesBwd / 2 - 1) / (kWavesBwd / 2);
@@ -439,28 +673,36 @@ hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStrea
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kWavesBwd * 64), lds, stream, a, k_in, v_in);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kWavesBwd * 64), lds, stream, a, rkey, rval,
+                     gcnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // 2. records grouped by table row, slot order kept inside a row
-  e = rocprim::radix_sort_pairs(tmp, tmp_bytes, k_in, k_out, v_in, v_out, (size_t)n, 0,
-                                (unsigned)end_bit, stream);
+  // 2. records grouped by table row, in group order inside a row: counts per
+  // (row, chunk), their exclusive scan, then the scatter
+  const dim3 cgrid((unsigned)q.nC, (unsigned)a.S);
+  hipLaunchKernelGGL(sdm_bwd_count_kernel, cgrid, dim3(256), (size_t)2 * a.n_sub * 4, stream, q,
+                     rkey, gcnt, offs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sdm_scan_sums_kernel, dim3((unsigned)nb), dim3(256), 0, stream, offs, M, bsum);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sdm_scan_top_kernel, dim3(1), dim3(256), 0, stream, bsum, (int)nb, offs + M);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sdm_scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, stream, offs, M, bsum);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t slds = scatter_lds_bytes(q);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(sdm_bwd_scatter_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
   if (e != hipSuccess) return e;
-  // 3. where each row's records start and end
-  const int cgrid = (int)std::min<int64_t>((2 * nkeys + 255) / 256, 4096);
-  hipLaunchKernelGGL(sdm_bwd_bounds_clear, dim3(cgrid), dim3(256), 0, stream, bounds, 2 * nkeys);
+  hipLaunchKernelGGL(sdm_bwd_scatter_kernel, cgrid, dim3(256), slds, stream, q, rkey, rval, gcnt,
+                     offs, vout);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int bgrid = (int)std::min<int64_t>((n + 255) / 256, 65536);
-  hipLaunchKernelGGL(sdm_bwd_bounds_kernel, dim3(bgrid), dim3(256), 0, stream, k_out, n,
-                     (uint32_t)nkeys, bounds);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // 4. one wave per table row
+  // 3. one wave per table row
   const unsigned rgrid = (unsigned)((nkeys + kRedWaves - 1) / kRedWaves);
   if (bf16)
     hipLaunchKernelGGL(sdm_score_bwd_reduce_kernel<true>, dim3(rgrid), dim3(kRedWaves * 64), 0,
-                       stream, a, v_out, bounds);
+                       stream, a, vout, offs, q.BnC);
   else
     hipLaunchKernelGGL(sdm_score_bwd_reduce_kernel<false>, dim3(rgrid), dim3(kRedWaves * 64), 0,
-                       stream, a, v_out, bounds);
+                       stream, a, vout, offs, q.BnC);
   return hipGetLastError();
 }
 
