@@ -541,6 +541,11 @@ def main():
                     help="run the scan in its time-parallel form (sdm_scan_timeparallel)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with tape + both backward calls)")
+    ap.add_argument("--streams", default=None, metavar="B,H",
+                    help="override the workload's batch and head counts (e.g. 1,1: one "
+                         "stream of its per-stream shape)")
+    ap.add_argument("--tokens", type=int, default=None, metavar="T",
+                    help="override the workload's tokens per stream")
     ap.add_argument("--cpu-streams", type=int, default=None,
                     help="streams in the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
@@ -575,6 +580,11 @@ def main():
     sdm.lib()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.config]
+    if args.streams:
+        b_, h_ = (int(v) for v in args.streams.split(","))
+        wl = wl.with_(B=b_, H=h_)
+    if args.tokens:
+        wl = wl.with_(T=args.tokens)
     if wl.name == "decode":
         bench_decode(args, wl, dev)
         return
@@ -595,6 +605,8 @@ def main():
     # single-threaded oracle sample sized for roughly 10-20 s of CPU work; the
     # all-core leg then runs every stream
     default_cpu = {"tiny": 1, "mid": 16, "large": 24, "long": 1, "gdn": 16}[wl.name]
+    if args.streams or args.tokens:
+        default_cpu = 0  # a resized workload: no oracle baseline unless asked
     n_cpu = args.cpu_streams if args.cpu_streams is not None else default_cpu
     n_cpu = min(n_cpu, wl.streams)
     host, m0s = None, None
@@ -680,7 +692,8 @@ def main():
         roof = {"bound": "hbm", "kernel": kname,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if args.timeparallel else measured_scan_traffic(wl),
+                "traffic": (None if args.timeparallel or args.streams or args.tokens
+                            else measured_scan_traffic(wl)),
                 "ms": round(ms_scan, 4), "bytes_per_launch": sbytes}
         allb = stream_tokens * (scan_bytes_per_token(wl) + score_bytes_per_token(wl))
         kernels = {"score_topk_ms": round(ms_score, 4), "scan_ms": round(ms_scan, 4),
