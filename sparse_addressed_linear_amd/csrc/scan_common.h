@@ -8,7 +8,9 @@ namespace scanc {
 
 constexpr uint64_t kEmpty = 0x00000000ffffffffull;  // LDS hash entry: key -1, empty mask
 
-// integer finaliser: a slot's hash for LDS tables and slot partitions
+// integer finaliser: a slot's hash for LDS tables and slot partitions.  The
+// shift/multiply constants are the published "lowbias32" finaliser of Chris
+// Wellons' hash-prospector search (a 32-bit xorshift-multiply mixer).
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   x *= 0x7feb352dU;
