@@ -496,7 +496,7 @@ def bench_raven(args, wl, dev):
            "table_GB": round(wl.table_bytes() / 1e9, 2)}
     if args.timeparallel:
         cfg["scan"] = "time-parallel"
-        roof["kernel"] = "sdm_scan_timeparallel (event keys, radix sort, slot segments, read sums)"
+        roof["kernel"] = "sdm_scan_timeparallel (slot sort, slot segments, read sums)"
     line = {"metric": "Routed selective-decay slots: stream-tokens/sec (router + scan)",
             "value": round(st / (ms_wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
@@ -687,7 +687,7 @@ def main():
         ms_scan = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
         sbytes = stream_tokens * scan_bytes_per_token(wl)
         achieved = sbytes / (ms_scan * 1e-3) / 1e9
-        kname = ("sdm_scan_timeparallel (event keys, radix sort, slot segments, read sums)"
+        kname = ("sdm_scan_timeparallel (slot sort, slot segments, read sums)"
                  if args.timeparallel else "sdm_scan (sdm_scan_kernel + sdm_partial_sum_kernel)")
         roof = {"bound": "hbm", "kernel": kname,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -209,13 +209,14 @@ size_t sdm_scan_workspace_size(const sdm_dims* dims);
  *
  * Arguments, layouts and results as sdm_scan, with this workspace:
  *   workspace  sdm_scan_timeparallel_workspace_size(dims) bytes, 256-byte
- *              aligned: sort keys and payloads (24 bytes per event, events =
- *              B*H*T*(W+R)), the sort's scratch and a read buffer of
- *              B*H*T*R*d_v floats.
+ *              aligned: two buffers of slots and positions (16 bytes per
+ *              event, events = B*H*T*(W+R)), the sort's digit counts (4
+ *              bytes per 4096 events per digit, at most 1024 digits) and a
+ *              read buffer of B*H*T*R*d_v floats.
  * The table and the outputs are bit-identical to the sequential scan's
- * definition (each element's fp32 operations in the same order).  Kernel
- * limits (else SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256];
- * B*H, N and T together within a 64-bit sort key; T*(W+R) < 2^32.
+ * definition (each element's fp32 operations in the same order).  Rows that
+ * only reads touch are not stored.  Kernel limits (else
+ * SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256]; B*H*T*(W+R) < 2^31.
  */
 int sdm_scan_timeparallel(const sdm_dims* dims, sdm_dtype v_dtype, float* M,
                           const int32_t* widx, const float* wwt, const int32_t* ridx,

@@ -39,6 +39,7 @@
 
 #include <algorithm>
 
+#include "excl_sum.h"
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -49,8 +50,7 @@ constexpr int kWavesBwd = 8;  // waves per workgroup (4 tokens x 2 sides)
 constexpr int kRedWaves = 4;  // waves per workgroup of the row sums
 constexpr int kChunks = 1024;  // counting-sort chunks a launch aims for
 constexpr int kStage = 1024;   // record slots of one scatter batch (256 threads x 4)
-constexpr int kScanPer = 16;  // elements per thread of the exclusive scan
-constexpr int kScanBlock = 256 * kScanPer;
+
 
 template <bool BF16>
 __device__ __forceinline__ float elem(const void* p, int64_t i) {
@@ -345,70 +345,6 @@ __global__ void __launch_bounds__(256) sdm_bwd_count_kernel(SortGeom q,
     cnt[((int64_t)h * nloc + l) * q.BnC + col] = hist[l];
 }
 
-// Exclusive scan of n int32 in place (x[n] receives the total), in blocks of
-// kScanBlock: block sums, a scan of the block sums by one workgroup, then each
-// block's own scan plus its offset.
-__device__ __forceinline__ int block_excl_scan256(int v, int* tmp) {
-  // exclusive prefix of v over the 256 threads of the block
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int inc = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) tmp[w] = inc;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; i++) before += tmp[i];
-  __syncthreads();
-  return before + inc - v;
-}
-
-__global__ void __launch_bounds__(256) sdm_scan_sums_kernel(const int32_t* __restrict__ x,
-                                                            int64_t n, int32_t* __restrict__ bsum) {
-  __shared__ int tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanPer;
-  int s = 0;
-  for (int i = 0; i < kScanPer; i++) s += base + i < n ? x[base + i] : 0;
-  const int ex = block_excl_scan256(s, tmp);
-  if (threadIdx.x == 255) bsum[blockIdx.x] = ex + s;
-}
-
-__global__ void __launch_bounds__(256) sdm_scan_top_kernel(int32_t* __restrict__ bsum, int nb,
-                                                           int32_t* __restrict__ total) {
-  __shared__ int tmp[4];
-  const int per = (nb + 255) / 256;
-  const int b0 = threadIdx.x * per;
-  int s = 0;
-  for (int i = 0; i < per; i++) s += b0 + i < nb ? bsum[b0 + i] : 0;
-  int run = block_excl_scan256(s, tmp);
-  for (int i = 0; i < per; i++) {
-    if (b0 + i < nb) {
-      const int v = bsum[b0 + i];
-      bsum[b0 + i] = run;
-      run += v;
-    }
-  }
-  if (threadIdx.x == 255) *total = run;
-}
-
-__global__ void __launch_bounds__(256) sdm_scan_down_kernel(int32_t* __restrict__ x, int64_t n,
-                                                            const int32_t* __restrict__ bsum) {
-  __shared__ int tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanPer;
-  int v[kScanPer];
-  int s = 0;
-  for (int i = 0; i < kScanPer; i++) {
-    v[i] = base + i < n ? x[base + i] : 0;
-    s += v[i];
-  }
-  int run = block_excl_scan256(s, tmp) + bsum[blockIdx.x];
-  for (int i = 0; i < kScanPer; i++) {
-    if (base + i < n) x[base + i] = run;
-    run += v[i];
-  }
-}
-
 // Scatter: the chunk's groups go in batches of up to 32, in order.  In a
 // batch, every record sets its group's bit in an LDS mask of its row (the
 // records of one group name distinct rows, and OR does not depend on the
@@ -639,10 +575,9 @@ size_t score_bwd_workspace_bytes(int S, int T, int H, int n_sub, int W, int R) {
   const int64_t n = score_bwd_records(S, T, W, R);
   const SortGeom q = sort_geom(S, T, H, n_sub, W, R);
   const int64_t M = (int64_t)H * 2 * n_sub * q.BnC;
-  const int64_t nb = (M + kScanBlock - 1) / kScanBlock;
   return align256((size_t)n * 4) + 2 * align256((size_t)n * 8) +
          align256((size_t)S * T * 4 * 4) + align256((size_t)(M + 1) * 4) +
-         align256((size_t)nb * 4);
+         align256((size_t)exsum::blocks(M) * 4);
 }
 
 hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStream_t stream) {
@@ -652,7 +587,6 @@ hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStrea
   const SortGeom q = sort_geom(a.S, a.T, a.H, a.n_sub, a.W, a.R);
   const int64_t nkeys = (int64_t)a.H * 2 * a.n_sub;
   const int64_t M = nkeys * q.BnC;
-  const int64_t nb = (M + kScanBlock - 1) / kScanBlock;
   unsigned char* p = static_cast<unsigned char*>(ws);
   uint32_t* rkey = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)n * 4);
@@ -682,12 +616,7 @@ hipError_t launch_score_bwd(const ScoreBwdArgs& a, bool bf16, void* ws, hipStrea
   hipLaunchKernelGGL(sdm_bwd_count_kernel, cgrid, dim3(256), (size_t)2 * a.n_sub * 4, stream, q,
                      rkey, gcnt, offs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sdm_scan_sums_kernel, dim3((unsigned)nb), dim3(256), 0, stream, offs, M, bsum);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sdm_scan_top_kernel, dim3(1), dim3(256), 0, stream, bsum, (int)nb, offs + M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sdm_scan_down_kernel, dim3((unsigned)nb), dim3(256), 0, stream, offs, M, bsum);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = exsum::run(offs, M, bsum, stream)) != hipSuccess) return e;
   const size_t slds = scatter_lds_bytes(q);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(sdm_bwd_scatter_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);

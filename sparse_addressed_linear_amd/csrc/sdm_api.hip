@@ -328,13 +328,11 @@ int sdm_scan_record(const sdm_dims* d, sdm_dtype v_dtype, float* M, const int32_
                   workspace, workspace_bytes, stream);
 }
 
-// time-parallel scan: whole rows per lane group, keys (stream, slot, t, kind)
-// in 64 bits, payload t*(W+R)+j in 32
+// time-parallel scan: whole rows per lane group (d_v/4 lanes), events of all
+// streams counted and placed in int32
 static int tp_shape_ok(const sdm_dims* d) {
-  const int64_t N = (int64_t)d->n_sub * d->n_sub;
   const bool dv_ok = d->d_v >= 16 && d->d_v <= 256 && (d->d_v & (d->d_v - 1)) == 0;
-  if (!dv_ok || sdm::tp_key_bits(d->B * d->H, d->T, N) > 64 ||
-      (int64_t)d->T * (d->W + d->R) >= (int64_t{1} << 32))
+  if (!dv_ok || !sdm::tp_sizes_ok(d->B * d->H, d->T, d->W, d->R))
     return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }

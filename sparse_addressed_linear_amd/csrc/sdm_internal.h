@@ -98,7 +98,7 @@ struct TpArgs {
   int32_t S, T, d_v, W, R;
 };
 
-int tp_key_bits(int S, int T, int64_t N);
+bool tp_sizes_ok(int S, int T, int W, int R);
 size_t tp_workspace_bytes(int S, int T, int64_t N, int d_v, int W, int R);
 hipError_t launch_scan_tp(const TpArgs& a, bool vbf16, void* ws, hipStream_t stream);
 

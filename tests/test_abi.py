@@ -255,8 +255,10 @@ def test_route_topk_rejects_before_any_launch(L):
 def test_scan_timeparallel_rejects_before_any_launch(L):
     d = dims(B=2, H=4, T=64, d_k=128, n_sub=256, d_v=64, W=32, R=32)
     need = L.sdm_scan_timeparallel_workspace_size(ctypes.byref(d))
-    # keys and payloads (24 bytes per event) plus the read buffer, at least
-    assert need >= 2 * 4 * 64 * 64 * 24 + 2 * 4 * 64 * 32 * 64 * 4
+    # two slot and position buffers (16 bytes per event), one digit count per
+    # 4096-event tile and digit (8-bit digits for N = 2^16), the read buffer
+    ev = 2 * 4 * 64 * 64
+    assert need >= ev * 16 + 2 * 4 * 256 * 4 + 2 * 4 * 64 * 32 * 64 * 4
 
     def tp(d, null_at=None, dt=0, ws=need, wsp=ctypes.c_void_p(4096), ptr=P):
         args = [ptr] * 9
@@ -272,6 +274,12 @@ def test_scan_timeparallel_rejects_before_any_launch(L):
     assert tp(d, wsp=ctypes.c_void_p(0)) == 7
     assert tp(d, wsp=ctypes.c_void_p(4112)) == 5   # not 256-byte aligned
     assert L.sdm_scan_timeparallel_workspace_size(ctypes.byref(dims(d_v=48))) == 0
+    # 2^31 events: places no longer fit int32
+    big = dims(B=1, H=1, T=1 << 24, d_k=128, n_sub=256, d_v=64, W=64, R=64)
+    assert L.sdm_scan_timeparallel_workspace_size(ctypes.byref(big)) == 0
+    assert tp(big) == 4
+    ok = dims(B=1, H=1, T=(1 << 24) - 1, d_k=128, n_sub=256, d_v=64, W=64, R=64)
+    assert L.sdm_scan_timeparallel_workspace_size(ctypes.byref(ok)) > 0
 
 
 def test_score_topk_noalloc_rejects_on_the_host(L):
