@@ -424,7 +424,9 @@ static hipError_t launch_scan_t(const ScanArgs& a, size_t lds, hipStream_t strea
 
 ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
   ScanPlan p{};
-  p.lpr = (d_v % 32 == 0) ? 8 : 4;
+  // row slices: whole 512 B rows where d_v allows (fewer workgroups share a
+  // token's index work; measured faster at d_v = 128), else 128 B, else 64 B
+  p.lpr = (d_v % 128 == 0) ? 32 : ((d_v % 32 == 0) ? 8 : 4);
   p.CS = d_v / (4 * p.lpr);
   // one token per stream (decoding): one-wave workgroups, so that several
   // share a CU and the launch runs in one round instead of idling 7 waves each
@@ -473,6 +475,9 @@ hipError_t launch_scan(const ScanArgs& a0, const ScanPlan& p, bool vbf16, hipStr
   } else
 #define SDM_SCAN_EPL(LPR_, MC_) \
   SDM_SCAN_CASE(LPR_, MC_, 8) SDM_SCAN_CASE(LPR_, MC_, 12) SDM_SCAN_CASE(LPR_, MC_, 16)
+  SDM_SCAN_EPL(32, 1)
+  SDM_SCAN_EPL(32, 2)
+  SDM_SCAN_EPL(32, 4)
   SDM_SCAN_EPL(8, 1)
   SDM_SCAN_EPL(8, 2)
   SDM_SCAN_EPL(8, 4)
