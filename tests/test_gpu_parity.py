@@ -203,6 +203,23 @@ def test_scan_vs_oracle(dev, label, args):
     check_scan(scan_case(dev, **args), label)
 
 
+def test_scan_table_over_2gib_per_stream(dev):
+    """A stream's table past 2^31 bytes (N = 1025^2, d_v = 512: 2.15 GB) is
+    scanned with plain 64-bit row addresses instead of 32-bit buffer offsets.
+    Half of every token's slots lie in the table's last 4096 rows, past the
+    2^31-byte mark; table bit-identical to the oracle's, outputs close."""
+    d = scan_case(dev, B=1, H=1, T=24, n_sub=1025, d_v=512, W=32, R=32, seed=13, hot=64)
+    N = 1025 * 1025
+    g = torch.Generator().manual_seed(14)
+    for key, k in (("widx", 32), ("ridx", 32)):
+        top = torch.stack([torch.randperm(4096, generator=g)[:k // 2] for _ in range(24)])
+        idx = d[key].cpu().clone()
+        idx[0, 0, :, : k // 2] = (N - 4096 + top).int()  # the rest stays in [0, 64)
+        d[key] = idx.to(dev)
+    assert int(d["widx"].max()) * 512 * 4 >= 1 << 31
+    check_scan(d, "table over 2 GiB per stream")
+
+
 def test_table_size_does_not_change_results(dev):
     """The same events on a 1024-slot table and on a 4096-slot table whose
     extra rows nothing touches (one slot partition at 160 streams either way):
