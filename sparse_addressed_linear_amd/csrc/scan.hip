@@ -5,14 +5,21 @@
 
 namespace sdm {
 
-// out[i] = sum over p of work[p][i], p ascending (deterministic).
+// out[i] = sum over p of work[p][i], p ascending (deterministic); the
+// partials are read once, as streaming loads.
 __global__ void __launch_bounds__(256) sdm_partial_sum_kernel(const float* __restrict__ work,
                                                               float* __restrict__ out,
                                                               int64_t n4, int P) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    float4 s = reinterpret_cast<const float4*>(work)[i];
-    for (int p = 1; p < P; p++) s = add4(s, reinterpret_cast<const float4*>(work)[p * n4 + i]);
+    const float* w0 = work + 4 * i;
+    float4 s = make_float4(__builtin_nontemporal_load(w0), __builtin_nontemporal_load(w0 + 1),
+                           __builtin_nontemporal_load(w0 + 2), __builtin_nontemporal_load(w0 + 3));
+    for (int p = 1; p < P; p++) {
+      const float* wp = work + 4 * (p * n4 + i);
+      s = add4(s, make_float4(__builtin_nontemporal_load(wp), __builtin_nontemporal_load(wp + 1),
+                              __builtin_nontemporal_load(wp + 2), __builtin_nontemporal_load(wp + 3)));
+    }
     reinterpret_cast<float4*>(out)[i] = s;
   }
 }

@@ -410,7 +410,12 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
     if (valid && g == 0) {
       float* dst = a.P == 1 ? a.out + trow * a.d_v + c0
                             : a.work + ((int64_t)pp * a.S * a.T + trow) * a.d_v + c0;
-      *reinterpret_cast<float4*>(dst) = acc;
+      // streamed past the caches (read once, by the partial sum) so that they
+      // do not displace table rows
+      __builtin_nontemporal_store(acc.x, dst + 0);
+      __builtin_nontemporal_store(acc.y, dst + 1);
+      __builtin_nontemporal_store(acc.z, dst + 2);
+      __builtin_nontemporal_store(acc.w, dst + 3);
     }
 
     // ---- 6. next block: compact, gates, indices after it, then its rows ---
