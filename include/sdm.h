@@ -175,10 +175,11 @@ int sdm_score_topk_packed(const sdm_dims* dims, sdm_dtype in_dtype, const void* 
  *                                        (may be NULL when that size is 0);
  *                                        its contents on entry do not matter.
  *
- * Slot indices must lie in [0, N) and the W write slots of one token must be
- * distinct; neither is checked on the device (an index outside [0, N) reads
- * and writes outside the stream's table).  Results are deterministic (the
- * read sums use a fixed order).  Scanning [0,T1) and then [T1,T) with the same
+ * An event whose slot lies outside [0, N) is ignored: nothing is read or
+ * written for it, so its write changes no row and its read adds nothing to
+ * the output (the table can never be touched outside the stream's rows).
+ * The W write slots of one token must be distinct (not checked).  Results
+ * are deterministic (the read sums use a fixed order).  Scanning [0,T1) and then [T1,T) with the same
  * M leaves a table bit-identical to one scan of [0,T), and bit-identical
  * outputs as well, except for tokens whose write plus read slots in one slot
  * partition exceed what a wave holds in registers (between 64 and 256 events,
@@ -205,7 +206,9 @@ size_t sdm_scan_workspace_size(const sdm_dims* dims);
  * (slot, time); each touched row is then loaded once, its writes applied in
  * time order, the row it holds at each read recorded, and each token's output
  * summed over its reads in rank order.  The parallelism is the number of
- * touched rows, not the number of streams.
+ * touched rows, not the number of streams.  Events whose slot lies outside
+ * [0, N) are ignored as in sdm_scan (such a read adds its weight times a
+ * zero row).
  *
  * Arguments, layouts and results as sdm_scan, with this workspace:
  *   workspace  sdm_scan_timeparallel_workspace_size(dims) bytes, 256-byte
@@ -273,7 +276,8 @@ int sdm_scan_record(const sdm_dims* dims, sdm_dtype v_dtype, float* M, const int
  * Write slots must be distinct within a token (as for sdm_scan); read slots
  * may repeat, and each read then adds its own share to the row's gradient (a
  * block of 8 tokens holding such a token is swept one read at a time, which
- * is slow but exact).
+ * is slow but exact).  Events whose slot lies outside [0, N) are skipped, as
+ * in the forward scan, and get dwwt / drwt = 0.
  * Results are deterministic.  The restored M equals M0 bit for bit (each
  * written row gets back its recorded value).  Kernel limits (else
  * SDM_ERR_UNSUPPORTED): d_v a power of two in [16, 256]; W, R <= 256.

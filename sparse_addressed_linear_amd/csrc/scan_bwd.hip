@@ -107,7 +107,12 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
   int32_t* sl = lslot + wave * a.lcap;
   float* wl = lwt + wave * a.lcap;
   int32_t* ml = lmeta + wave * a.lcap;
-  auto in_part = [&](int32_t s) { return ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp; };
+  // an event whose slot lies outside [0, N) belongs to no partition (the
+  // forward scan ignored it); partition 0 gives its weight a zero gradient
+  const uint32_t nlim = (uint32_t)a.N;
+  auto in_part = [&](int32_t s) {
+    return (uint32_t)s < nlim && ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp;
+  };
   const uint64_t below = (1ull << lane) - 1ull;
 
   for (int i = tid; i < a.hsize; i += NT) htab[i] = kEmpty;
@@ -158,6 +163,7 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
         if (c * 64 < a.R) {
           const int i = c * 64 + lane;
           const bool f = i < a.R && in_part(qs[c]);
+          if (pp == 0 && i < a.R && (uint32_t)qs[c] >= nlim) a.drwt[trow * a.R + i] = 0.f;
           const uint64_t bal = __ballot(f);
           if (f) {
             const int pos = nr + __popcll(bal & below);
@@ -173,6 +179,7 @@ __global__ void __launch_bounds__(kNW * 64, 1) sdm_scan_bwd_kernel(ScanBwdArgs a
         if (c * 64 < a.W) {
           const int i = c * 64 + lane;
           const bool f = i < a.W && in_part(ps[c]);
+          if (pp == 0 && i < a.W && (uint32_t)ps[c] >= nlim) a.dwwt[trow * a.W + i] = 0.f;
           const uint64_t bal = __ballot(f);
           if (f) {
             const int pos = nr + nwr + __popcll(bal & below);

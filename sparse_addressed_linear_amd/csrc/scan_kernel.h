@@ -162,7 +162,12 @@ __global__ void __launch_bounds__(NW * 64, 1) sdm_scan_kernel(ScanArgs a) {
     if constexpr (TAPE)
       *reinterpret_cast<float4*>(a.tape + (trow * a.W + (ml[e] >> 8)) * a.d_v + c0) = x;
   };
-  auto in_part = [&](int32_t s) { return ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp; };
+  // an event whose slot lies outside [0, N) belongs to no partition: it is
+  // neither read nor written
+  const uint32_t nlim = (uint32_t)a.N;
+  auto in_part = [&](int32_t s) {
+    return (uint32_t)s < nlim && ((mix32((uint32_t)s) >> 16) & pmask) == (uint32_t)pp;
+  };
 
   // ---- index prefetch for one token (registers; unconditional loads) -----
   int32_t ps[MC], qs[MC];

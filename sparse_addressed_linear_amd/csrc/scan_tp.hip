@@ -57,6 +57,18 @@ __device__ __forceinline__ uint32_t event_slot(const TpArgs& a, int64_t st, int6
   return (uint32_t)(j < a.W ? a.widx[tok * a.W + j] : a.ridx[tok * a.R + (j - a.W)]);
 }
 
+// An event whose slot lies outside [0, N) is ignored: it sorts as slot 0 with
+// kIgnored set in its payload, writes nothing and reads a zero row.
+constexpr uint32_t kIgnored = 0x80000000u;
+
+__device__ __forceinline__ void first_pass_event(const TpArgs& a, int64_t st, int64_t p,
+                                                 uint32_t& key, uint32_t& val) {
+  const uint32_t s = event_slot(a, st, p);
+  const bool ok = s < (uint32_t)a.N;
+  key = ok ? s : 0u;
+  val = ok ? (uint32_t)p : ((uint32_t)p | kIgnored);
+}
+
 // 1a. digit counts of each tile: gh[(stream*rad + digit)*tps + tile].  One
 // wave per tile with its own LDS counts; the first pass reads the slots from
 // the index lists, later ones the previous pass's output.
@@ -79,7 +91,9 @@ __global__ void __launch_bounds__(256) sdm_tp_hist_kernel(TpArgs a, SortPass sp,
 #pragma unroll
     for (int u = 0; u < kU; u++) {
       const int64_t p = p0 + 64 * u;
-      k[u] = p < t1 ? (FIRST ? event_slot(a, st, p) : kin[st * sp.L + p]) : 0u;
+      uint32_t kf = 0u, vf;
+      if (FIRST && p < t1) first_pass_event(a, st, p, kf, vf);
+      k[u] = p < t1 ? (FIRST ? kf : kin[st * sp.L + p]) : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kU; u++)
@@ -121,8 +135,10 @@ __global__ void __launch_bounds__(256) sdm_tp_scatter_kernel(
   for (int u = 0; u < kU; u++) {
     const int64_t p = t0 + (int64_t)(wave * kU + u) * 64 + lane;
     const bool on = p < t1;
-    k[u] = on ? (FIRST ? event_slot(a, st, p) : kin[st * sp.L + p]) : 0u;
-    v[u] = on ? (FIRST ? (uint32_t)p : vin[st * sp.L + p]) : 0u;
+    uint32_t kf = 0u, vf = 0u;
+    if (FIRST && on) first_pass_event(a, st, p, kf, vf);
+    k[u] = on ? (FIRST ? kf : kin[st * sp.L + p]) : 0u;
+    v[u] = on ? (FIRST ? vf : vin[st * sp.L + p]) : 0u;
   }
   const int per = rad > 256 ? rad / 256 : 1;
   int gs[kPer];
@@ -240,20 +256,25 @@ __global__ void __launch_bounds__(256) sdm_tp_segments_kernel(TpArgs a, const ui
     const int64_t st1 = cross ? st + 1 : st;
     float* row1 = next_here ? rowp(st1, k1) : row;
     const float4 mnext = *reinterpret_cast<const float4*>(row1);  // (row itself if unused)
-    const int t = (int)(pj / WR), r = (int)(pj - (uint32_t)t * WR);
+    const bool ign = (pj & kIgnored) != 0u;
+    const uint32_t pos = pj & ~kIgnored;
+    const int t = (int)(pos / WR), r = (int)(pos - (uint32_t)t * WR);
     const int64_t tok = st * a.T + t;
     if (r < a.W) {
-      const float c = a.beta[tok] * a.wwt[tok * a.W + r];
-      const float omc = 1.0f - c;
-      const float al = a.alpha[tok];
-      const float4 v = load_v4(a.v, VBF16, tok * a.d_v + c0);
-      m.x = omc * (al * m.x) + c * v.x;
-      m.y = omc * (al * m.y) + c * v.y;
-      m.z = omc * (al * m.z) + c * v.z;
-      m.w = omc * (al * m.w) + c * v.w;
-      dirty = true;
+      if (!ign) {
+        const float c = a.beta[tok] * a.wwt[tok * a.W + r];
+        const float omc = 1.0f - c;
+        const float al = a.alpha[tok];
+        const float4 v = load_v4(a.v, VBF16, tok * a.d_v + c0);
+        m.x = omc * (al * m.x) + c * v.x;
+        m.y = omc * (al * m.y) + c * v.y;
+        m.z = omc * (al * m.z) + c * v.z;
+        m.w = omc * (al * m.w) + c * v.w;
+        dirty = true;
+      }
     } else {
-      *reinterpret_cast<float4*>(readbuf + (tok * a.R + (r - a.W)) * a.d_v + c0) = m;
+      *reinterpret_cast<float4*>(readbuf + (tok * a.R + (r - a.W)) * a.d_v + c0) =
+          ign ? make_float4(0.f, 0.f, 0.f, 0.f) : m;
     }
     if (ends) {
       if (dirty) *reinterpret_cast<float4*>(row) = m;

@@ -250,3 +250,33 @@ def e2e_stream(g_lists, ref, xk, xq, C, Mg, M_ref, og, o_ref, msg=""):
     return E2ETally(streams=1, w=tw, r=tr, flagged_streams=int(bool(tw.flagged or tr.flagged)),
                     outs=T, outs_compared=int(out_ok.sum()), rows=N,
                     rows_compared=int(row_ok.sum()))
+
+
+def ignored_events(lists, N, sink0, seed, frac=0.1):
+    """Slot lists with about `frac` of the events given a slot outside
+    [0, N) (-1, -2^31, 2^31 - 1, N or N + 7), which the scans ignore, and the
+    oracle's equivalent: those writes write the distinct sink slots
+    sink0 + rank and those reads read slot sink0 with weight 0, which
+    changes rows [sink0, N) only.  Every valid slot must be below sink0 and
+    N - sink0 >= W.  `lists` maps widx, wwt, ridx, rwt to CPU tensors;
+    returns (gpu_lists, oracle_lists, {"widx": mask, "ridx": mask})."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    bad_vals = torch.tensor([-1, -(1 << 31), (1 << 31) - 1, N, N + 7], dtype=torch.int32)
+    gpu, ref, masks = dict(lists), dict(lists), {}
+    for key, wkey in (("widx", "wwt"), ("ridx", "rwt")):
+        idx = lists[key]
+        assert int(idx.max()) < sink0
+        mask = torch.rand(idx.shape, generator=g) < frac
+        bad = bad_vals[torch.randint(0, len(bad_vals), idx.shape, generator=g)]
+        gpu[key] = torch.where(mask, bad, idx).contiguous()
+        if key == "widx":
+            k = idx.shape[-1]
+            assert N - sink0 >= k
+            sink = (sink0 + torch.arange(k, dtype=torch.int32)).expand(idx.shape)
+            ref[key] = torch.where(mask, sink, idx).contiguous()
+        else:
+            ref[key] = torch.where(mask, torch.full_like(idx, sink0), idx).contiguous()
+            ref[wkey] = torch.where(mask, torch.zeros_like(lists[wkey]), lists[wkey]).contiguous()
+        masks[key] = mask
+    return gpu, ref, masks

@@ -19,7 +19,7 @@ import torch
 import oracle
 import synth
 from oracle import backward as ob
-from gpu_util import np_, say
+from gpu_util import ignored_events, np_, say
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +139,38 @@ def test_scan_backward_vs_oracle(dev, label, args):
     for b, h in {(0, 0), (B - 1, H - 1)}:
         assert np.array_equal(np_(tape[b, h]), oracle_tape(d, b, h)), "tape differs"
         check_stream(d, g, dM, b, h, label)
+
+
+def test_scan_backward_ignores_slots_outside_the_table(dev):
+    """Events whose slot lies outside [0, N) are skipped by the recorded
+    forward and by the reverse sweep, and their weight gradients are 0.
+    Oracle: those writes go to sink rows [200, 256) and those reads get
+    weight 0, with dL/dM_T zero on the sink rows, so every gradient is the
+    same; only the oracle's drwt of the weight-0 reads (row . dO) is not
+    compared (the GPU's is 0)."""
+    N, sink0 = 256, 200
+    d = scan_inputs(B=2, H=2, T=57, n_sub=16, d_v=64, W=16, R=16, seed=30, hot=sink0)
+    d["dMT"][:, :, sink0:] = 0.0
+    gpu_l, ref_l, masks = ignored_events(d, N, sink0, seed=31)
+    assert masks["widx"].any() and masks["ridx"].any()
+    dg = dict(d, **{k: gpu_l[k] for k in ("widx", "ridx")})
+    x, M, dM, g, tape, out = run_gpu_scan_grads(dg, dev)
+    assert torch.equal(M, x["M0"]), "table not restored to M0"
+    dr = dict(d, **ref_l)
+    for b, h in ((0, 0), (1, 1)):
+        sl = (b, h)
+        ref = ob.scan_backward_stream(np_(dr["M0"][sl]), np_(dr["widx"][sl]), np_(dr["wwt"][sl]),
+                                      np_(dr["ridx"][sl]), np_(dr["rwt"][sl]), np_(dr["v"][sl]),
+                                      np_(dr["alpha"][sl]), np_(dr["beta"][sl]),
+                                      np_(dr["dout"][sl]), np_(dr["dMT"][sl]))
+        label = f"ignored slots stream {b},{h}"
+        grad_close(np_(dM[sl]), ref["dM0"], f"{label} dM0")
+        for key in ("dv", "dalpha", "dbeta", "dwwt"):
+            grad_close(np_(g[key][sl]), ref[key], f"{label} {key}")
+        mr = masks["ridx"][sl].numpy()
+        assert np.all(np_(g["drwt"][sl])[mr] == 0.0), f"{label}: ignored reads' drwt not 0"
+        assert np.all(np_(g["dwwt"][sl])[masks["widx"][sl].numpy()] == 0.0)
+        grad_close(np_(g["drwt"][sl])[~mr], ref["drwt"][~mr], f"{label} drwt")
 
 
 def test_score_backward_vs_oracle(dev):

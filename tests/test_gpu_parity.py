@@ -25,7 +25,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import E2ETally, close, compare_topk, e2e_stream, np_, say, thread_map
+from gpu_util import (E2ETally, close, compare_topk, e2e_stream, ignored_events, np_, say,
+                      thread_map)
 
 pytestmark = pytest.mark.gpu
 
@@ -201,6 +202,38 @@ def check_scan(d, label):
 ])
 def test_scan_vs_oracle(dev, label, args):
     check_scan(scan_case(dev, **args), label)
+
+
+def test_scans_ignore_slots_outside_the_table(dev):
+    """Events whose slot lies outside [0, N) are neither read nor written by
+    the sequential or the time-parallel scan.  Against the oracle run with
+    those writes sent to sink rows [960, 1024) and those reads given weight
+    0: rows [0, 960) bit-identical, the sink rows untouched (still M0),
+    outputs close (sequential) or equal (time-parallel)."""
+    N, sink0 = 1024, 960
+    d = scan_case(dev, B=2, H=2, T=70, n_sub=32, d_v=64, W=16, R=16, seed=16, hot=sink0)
+    cpu = {k: d[k].cpu() for k in ("widx", "wwt", "ridx", "rwt")}
+    gpu_l, ref_l, masks = ignored_events(cpu, N, sink0, seed=17)
+    assert masks["widx"].any() and masks["ridx"].any()
+    M_ref = np_(d["M0"]).copy()
+    out_ref = oracle.scan(M_ref, *(np_(ref_l[k]) for k in ("widx", "wwt", "ridx", "rwt")),
+                          np_(d["v"]), np_(d["alpha"]), np_(d["beta"]))
+    g = [gpu_l[k].to(dev) for k in ("widx", "wwt", "ridx", "rwt")]
+    M0 = np_(d["M0"])
+    for name, fn in (("sequential", sdm().scan), ("time-parallel", sdm().scan_timeparallel)):
+        say(f"case: {name} scan with slots outside the table")
+        M = d["M0"].clone()
+        out = fn(M, *g, d["v"], d["alpha"], d["beta"])
+        torch.cuda.synchronize()
+        Mg = np_(M)
+        assert np.array_equal(Mg[:, :, :sink0].view(np.uint32),
+                              M_ref[:, :, :sink0].view(np.uint32)), f"{name}: table differs"
+        assert np.array_equal(Mg[:, :, sink0:].view(np.uint32),
+                              M0[:, :, sink0:].view(np.uint32)), f"{name}: sink rows touched"
+        if name == "sequential":
+            assert np.all(close(np_(out), out_ref)), f"{name}: outputs differ"
+        else:
+            assert np.array_equal(np_(out), out_ref), f"{name}: outputs differ"
 
 
 def test_scan_table_over_2gib_per_stream(dev):
