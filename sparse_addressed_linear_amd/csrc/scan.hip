@@ -26,20 +26,33 @@ __global__ void __launch_bounds__(256) sdm_partial_sum_kernel(const float* __res
 
 ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
   ScanPlan p{};
-  // row slices: whole 512 B rows where d_v allows (fewer workgroups share a
-  // token's index work; measured faster at d_v = 128), else 128 B, else 64 B
-  p.lpr = (d_v % 128 == 0) ? 32 : ((d_v % 32 == 0) ? 8 : 4);
+  // partitions for cs column slices: enough workgroups to occupy every CU,
+  // while keeping enough events per token and partition to fill a wave
+  auto parts = [&](int cs) {
+    int P = 1;
+    while (P < 64 && (int64_t)S * cs * (P * 2) <= kTargetWorkgroups &&
+           (W + R) / (P * 2) >= 8 && P * 2 <= N)
+      P *= 2;
+    return P;
+  };
+  // row slices: 128 B (64 B where d_v is not a multiple of 32), or whole
+  // 512 B slices where d_v is a multiple of 128 and they still fill the GPU
+  // with few partitions, at most (2W+R)/24, so that the partial read sums add
+  // at most about 8% to the scan's bytes.  Whole rows mean fewer, larger row
+  // accesses per workgroup: measured faster at d_v = 128 with 16 streams,
+  // slower with 8 (32 partitions)
+  p.lpr = d_v % 32 == 0 ? 8 : 4;
+  if (d_v % 128 == 0) {
+    const int cs = d_v / 128;
+    const int pw = parts(cs);
+    if ((int64_t)S * cs * pw >= kTargetWorkgroups && pw * 24 <= 2 * W + R) p.lpr = 32;
+  }
   p.CS = d_v / (4 * p.lpr);
+  p.P = parts(p.CS);
+  const int P = p.P;
   // one token per stream (decoding): one-wave workgroups, so that several
   // share a CU and the launch runs in one round instead of idling 7 waves each
   p.nw = (T == 1 && !tape) ? 1 : 8;
-  // partitions: enough workgroups to occupy every CU, while keeping enough
-  // events per token and partition to fill a wave.
-  int P = 1;
-  while (P < 64 && (int64_t)S * p.CS * (P * 2) <= kTargetWorkgroups &&
-         (W + R) / (P * 2) >= 8 && P * 2 <= N)
-    P *= 2;
-  p.P = P;
   // registers per lane group: the mean events of a token in one partition
   // plus four standard deviations (partitions are hashed, so the count is
   // close to binomial); rarer tokens take the overflow path

@@ -193,10 +193,14 @@ def check_scan(d, label):
     ("small table, d_v=512, W=R=128", dict(B=2, H=2, T=40, n_sub=32, d_v=512, W=128, R=128,
                                        seed=6, hot=300)),
     ("W=256, R=200", dict(B=1, H=2, T=20, n_sub=32, d_v=32, W=256, R=200, seed=8)),
-    ("d_v=128 whole rows, partitions", dict(B=2, H=2, T=97, n_sub=64, d_v=128, W=64, R=64,
-                                            seed=10)),
-    ("d_v=256 whole rows, hot, bf16 v", dict(B=1, H=2, T=60, n_sub=32, d_v=256, W=32, R=48,
-                                             seed=11, hot=120, v_bf16=True)),
+    ("d_v=128, partitions", dict(B=2, H=2, T=97, n_sub=64, d_v=128, W=64, R=64, seed=10)),
+    ("d_v=256, hot, bf16 v", dict(B=1, H=2, T=60, n_sub=32, d_v=256, W=32, R=48, seed=11,
+                                  hot=120, v_bf16=True)),
+    # 16 streams of d_v = 128 with W = R = 128 take whole 512 B rows in 16 partitions
+    ("whole rows, 16 streams", dict(B=4, H=4, T=40, n_sub=32, d_v=128, W=128, R=128, seed=18,
+                                    hot=600)),
+    ("whole rows, 16 streams, bf16 v, T=1", dict(B=4, H=4, T=1, n_sub=32, d_v=128, W=128,
+                                                 R=128, seed=19, v_bf16=True)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=64, d_v=32, W=4, R=4, seed=7)),
     ("small table, T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
 ])
