@@ -28,10 +28,11 @@ class Dims(ctypes.Structure):
 
 
 def lib():
-    """Load (building first if needed) the oracle library."""
+    """Load (building first if needed) the oracle library, or the build named
+    by SDM_ORACLE_LIB (an instrumented one, for the sanitizer test)."""
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        path = os.environ.get("SDM_ORACLE_LIB") or _build.build(force=False)
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32 = ctypes.c_int32

@@ -15,15 +15,16 @@ CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fno-builti
           "-Wall", "-Wextra", "-shared", "-fPIC"]
 
 
-def build(force: bool = True, extra_flags=()) -> str:
-    """Build the oracle library; returns its path."""
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
-        return LIB
-    tmp = LIB + ".tmp"
+def build(force: bool = True, extra_flags=(), out: str = LIB) -> str:
+    """Build the oracle library (at `out`, by default oracle/libsdm_oracle.so);
+    returns its path."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+        return out
+    tmp = out + ".tmp"
     cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
