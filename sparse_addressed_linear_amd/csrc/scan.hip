@@ -35,17 +35,34 @@ ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
       P *= 2;
     return P;
   };
-  // row slices: 128 B (64 B where d_v is not a multiple of 32), or whole
-  // 512 B slices where d_v is a multiple of 128 and they still fill the GPU
-  // with few partitions, at most (2W+R)/24, so that the partial read sums add
-  // at most about 8% to the scan's bytes.  Whole rows mean fewer, larger row
-  // accesses per workgroup: measured faster at d_v = 128 with 16 streams,
-  // slower with 8 (32 partitions)
+  // registers per lane group for P partitions and lanes-per-slice lpr: the
+  // mean events of a token in one partition plus three standard deviations
+  // (partitions are hashed, so the count is close to binomial); rarer tokens
+  // take the overflow path, which costs little at that rate
+  auto epl_for = [&](int P, int lpr) {
+    const double mean = (double)(W + R) / P;
+    const double need = mean + 3.0 * sqrt(mean * (1.0 - 1.0 / P)) + 1.0;
+    const int gpw = 64 / lpr;
+    return need <= 8 * gpw ? 8 : (need <= 12 * gpw ? 12 : (need <= 16 * gpw ? 16 : 0));
+  };
+  // row slices: 128 B (64 B where d_v is not a multiple of 32), or wider ones
+  // -- 512 B, else 256 B -- where d_v allows and they still fill the GPU with
+  // few partitions, at most (2W+R)/24, so that the partial read sums add at
+  // most about 8% to the scan's bytes, and a token's events of a partition
+  // still fit a wave's registers.  Wider slices mean fewer workgroups repeat
+  // a token's index work and fewer, larger row accesses per workgroup:
+  // measured faster with whole 256 B rows at Large and whole 512 B rows at
+  // Long (16 streams), slower with 32 partitions (8 of Long's streams)
   p.lpr = d_v % 32 == 0 ? 8 : 4;
-  if (d_v % 128 == 0) {
-    const int cs = d_v / 128;
+  for (const int lpr : {32, 16}) {
+    if (d_v % (4 * lpr)) continue;
+    const int cs = d_v / (4 * lpr);
     const int pw = parts(cs);
-    if ((int64_t)S * cs * pw >= kTargetWorkgroups && pw * 24 <= 2 * W + R) p.lpr = 32;
+    if ((int64_t)S * cs * pw >= kTargetWorkgroups && pw * 24 <= 2 * W + R &&
+        epl_for(pw, lpr) != 0) {
+      p.lpr = lpr;
+      break;
+    }
   }
   p.CS = d_v / (4 * p.lpr);
   p.P = parts(p.CS);
@@ -53,13 +70,8 @@ ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
   // one token per stream (decoding): one-wave workgroups, so that several
   // share a CU and the launch runs in one round instead of idling 7 waves each
   p.nw = (T == 1 && !tape) ? 1 : 8;
-  // registers per lane group: the mean events of a token in one partition
-  // plus four standard deviations (partitions are hashed, so the count is
-  // close to binomial); rarer tokens take the overflow path
-  const double mean = (double)(W + R) / P;
-  const double need = mean + 4.0 * sqrt(mean * (1.0 - 1.0 / P)) + 1.0;
-  const int gpw = 64 / p.lpr;
-  p.epl = need <= 8 * gpw ? 8 : (need <= 12 * gpw ? 12 : 16);
+  p.epl = epl_for(P, p.lpr);
+  if (p.epl == 0) p.epl = 16;  // most tokens take the overflow path
   int64_t hs = 1;
   while (hs < 2LL * p.nw * W) hs *= 2;
   p.hsize = (int)hs;

@@ -474,6 +474,9 @@ hipError_t launch_scan_kernel(const ScanArgs& a, const ScanPlan& p, bool vbf16,
   SDM_SCAN_EPL(32, 1)
   SDM_SCAN_EPL(32, 2)
   SDM_SCAN_EPL(32, 4)
+  SDM_SCAN_EPL(16, 1)
+  SDM_SCAN_EPL(16, 2)
+  SDM_SCAN_EPL(16, 4)
   SDM_SCAN_EPL(8, 1)
   SDM_SCAN_EPL(8, 2)
   SDM_SCAN_EPL(8, 4)
