@@ -38,31 +38,30 @@ ScanPlan plan_scan(int S, int T, int64_t N, int d_v, int W, int R, bool tape) {
   // registers per lane group for P partitions and lanes-per-slice lpr: the
   // mean events of a token in one partition plus three standard deviations
   // (partitions are hashed, so the count is close to binomial); rarer tokens
-  // take the overflow path, which costs little at that rate
+  // take the overflow path, which costs little at that rate, while every
+  // register slot past a token's events is a padding load
   auto epl_for = [&](int P, int lpr) {
     const double mean = (double)(W + R) / P;
-    const double need = mean + 3.0 * sqrt(mean * (1.0 - 1.0 / P)) + 1.0;
+    const double need = mean + 3.0 * sqrt(mean * (1.0 - 1.0 / P));
     const int gpw = 64 / lpr;
     return need <= 8 * gpw ? 8 : (need <= 12 * gpw ? 12 : (need <= 16 * gpw ? 16 : 0));
   };
-  // row slices: 128 B (64 B where d_v is not a multiple of 32), or wider ones
-  // -- 512 B, else 256 B -- where d_v allows and they still fill the GPU with
-  // few partitions, at most (2W+R)/24, so that the partial read sums add at
-  // most about 8% to the scan's bytes, and a token's events of a partition
-  // still fit a wave's registers.  Wider slices mean fewer workgroups repeat
-  // a token's index work and fewer, larger row accesses per workgroup:
-  // measured faster with whole 256 B rows at Large and whole 512 B rows at
-  // Long (16 streams), slower with 32 partitions (8 of Long's streams)
+  // row slices: 128 B (64 B where d_v is not a multiple of 32), or 256 B
+  // where d_v allows and they still fill the GPU with few partitions, at most
+  // (2W+R)/24, so that the partial read sums add at most about 8% to the
+  // scan's bytes, and a token's events of a partition still fit a wave's
+  // registers.  Wider slices mean fewer workgroups repeat a token's index work
+  // and fewer, larger row accesses per workgroup.  Measured (same box): Large
+  // 2.86 ms with 256 B slices against 3.14 with 128 B; Long 50.3 ms against
+  // 55.9 with 128 B and 52.9 with whole 512 B rows (16 partitions, half the
+  // register slots padding)
   p.lpr = d_v % 32 == 0 ? 8 : 4;
-  for (const int lpr : {32, 16}) {
-    if (d_v % (4 * lpr)) continue;
-    const int cs = d_v / (4 * lpr);
+  if (d_v % 64 == 0) {
+    const int cs = d_v / 64;
     const int pw = parts(cs);
     if ((int64_t)S * cs * pw >= kTargetWorkgroups && pw * 24 <= 2 * W + R &&
-        epl_for(pw, lpr) != 0) {
-      p.lpr = lpr;
-      break;
-    }
+        epl_for(pw, 16) != 0)
+      p.lpr = 16;
   }
   p.CS = d_v / (4 * p.lpr);
   p.P = parts(p.CS);

@@ -471,9 +471,6 @@ hipError_t launch_scan_kernel(const ScanArgs& a, const ScanPlan& p, bool vbf16,
   } else
 #define SDM_SCAN_EPL(LPR_, MC_) \
   SDM_SCAN_CASE(LPR_, MC_, 8) SDM_SCAN_CASE(LPR_, MC_, 12) SDM_SCAN_CASE(LPR_, MC_, 16)
-  SDM_SCAN_EPL(32, 1)
-  SDM_SCAN_EPL(32, 2)
-  SDM_SCAN_EPL(32, 4)
   SDM_SCAN_EPL(16, 1)
   SDM_SCAN_EPL(16, 2)
   SDM_SCAN_EPL(16, 4)

@@ -304,19 +304,19 @@ def test_score_topk_noalloc_rejects_on_the_host(L):
 
 def test_scan_plan_partitions(L):
     """The scan's slot partitions, read off its workspace (P partial read sums
-    of B*H*T*d_v floats when P > 1): whole 256 B rows at Large (P = 4), whole
-    512 B rows for Long's 16 streams (P = 16), 256 B slices for 8 streams of
-    Long's shape (P = 16; whole rows would need 32 partitions, more than
-    (2W+R)/24), 128 B slices where wider ones cannot fill the GPU (4 streams
-    of Long's shape, Mid) and for decoding (a token's 128 events of one
-    partition would not fit a wave of 256 B slices)."""
+    of B*H*T*d_v floats when P > 1): 256 B row slices at Large (whole rows,
+    P = 4), for Long's 16 streams (P = 8) and for 8 streams of Long's shape
+    (P = 16, within (2W+R)/24 partitions); 128 B slices where 256 B ones
+    cannot fill the GPU (4 streams of Long's shape, Mid) and for decoding
+    (a token's 128 events of one partition would not fit a wave of 256 B
+    slices)."""
     def parts(**kw):
         d = dims(**kw)
         return L.sdm_scan_workspace_size(ctypes.byref(d)) / (d.B * d.H * d.T * d.d_v * 4)
     assert parts(B=8, H=8, T=4096, d_k=128, n_sub=1024, d_v=64, W=64, R=64) == 4
-    assert parts(B=1, H=16, T=65536, d_k=256, n_sub=1024, d_v=128, W=128, R=128) == 16
+    assert parts(B=1, H=16, T=65536, d_k=256, n_sub=1024, d_v=128, W=128, R=128) == 8
     assert parts(B=1, H=8, T=65536, d_k=256, n_sub=1024, d_v=128, W=128, R=128) == 16
     assert parts(B=1, H=4, T=65536, d_k=256, n_sub=1024, d_v=128, W=128, R=128) == 16
     assert parts(B=4, H=4, T=2048, d_k=128, n_sub=256, d_v=64, W=32, R=32) == 8
     assert parts(B=256, H=1, T=1, d_k=128, n_sub=1024, d_v=64, W=64, R=64) == 0
-    assert parts(B=4, H=4, T=40, d_k=32, n_sub=32, d_v=128, W=128, R=128) == 16
+    assert parts(B=4, H=4, T=40, d_k=32, n_sub=32, d_v=128, W=128, R=128) == 8

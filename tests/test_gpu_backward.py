@@ -125,7 +125,7 @@ def check_stream(d, g, dM, b, h, label):
     ("hot W=1", dict(B=1, H=1, T=150, n_sub=8, d_v=32, W=1, R=3, seed=25, hot=4)),
     ("serial path", dict(B=2, H=2, T=30, n_sub=32, d_v=256, W=128, R=128, seed=26, hot=300)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=27)),
-    ("whole-row forward, 16 streams", dict(B=4, H=4, T=24, n_sub=32, d_v=128, W=128, R=128,
+    ("256 B slice forward, 16 streams", dict(B=4, H=4, T=24, n_sub=32, d_v=128, W=128, R=128,
                                            seed=32, hot=600)),
     ("repeated read slots", dict(B=1, H=2, T=33, n_sub=16, d_v=32, W=8, R=8, seed=28, hot=40,
                                  repeat_reads=True)),

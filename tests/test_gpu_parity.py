@@ -196,16 +196,48 @@ def check_scan(d, label):
     ("d_v=128, partitions", dict(B=2, H=2, T=97, n_sub=64, d_v=128, W=64, R=64, seed=10)),
     ("d_v=256, hot, bf16 v", dict(B=1, H=2, T=60, n_sub=32, d_v=256, W=32, R=48, seed=11,
                                   hot=120, v_bf16=True)),
-    # 16 streams of d_v = 128 with W = R = 128 take whole 512 B rows in 16 partitions
-    ("whole rows, 16 streams", dict(B=4, H=4, T=40, n_sub=32, d_v=128, W=128, R=128, seed=18,
-                                    hot=600)),
-    ("whole rows, 16 streams, bf16 v, T=1", dict(B=4, H=4, T=1, n_sub=32, d_v=128, W=128,
-                                                 R=128, seed=19, v_bf16=True)),
+    # 16 streams of d_v = 128 with W = R = 128 take 256 B slices in 8 partitions
+    ("256 B slices, 16 streams", dict(B=4, H=4, T=40, n_sub=32, d_v=128, W=128, R=128, seed=18,
+                                      hot=600)),
+    ("256 B slices, 16 streams, bf16 v, T=1", dict(B=4, H=4, T=1, n_sub=32, d_v=128, W=128,
+                                                   R=128, seed=19, v_bf16=True)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=64, d_v=32, W=4, R=4, seed=7)),
     ("small table, T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
 ])
 def test_scan_vs_oracle(dev, label, args):
     check_scan(scan_case(dev, **args), label)
+
+
+def _partition_hash(x):
+    """The scan's slot-partition hash (lowbias32), used here only to build an
+    input that piles every event into one partition."""
+    x ^= x >> 16
+    x = (x * 0x7FEB352D) & 0xFFFFFFFF
+    x ^= x >> 15
+    x = (x * 0x846CA68B) & 0xFFFFFFFF
+    x ^= x >> 16
+    return x
+
+
+def test_scan_overflow_with_256b_slices(dev):
+    """64 streams of d_v = 64 with W = R = 64 take whole 256 B rows in 4
+    partitions, 48 register slots per token and partition.  Every slot here
+    falls in partition 0, so each token's 128 events overflow the registers
+    and every block takes the overflow path: table bit-identical, outputs
+    close."""
+    import ctypes
+    import sparse_addressed_linear_amd as m
+    dims = m.Dims(8, 8, 24, 2, 32, 64, 64, 64)
+    assert m.lib().sdm_scan_workspace_size(ctypes.byref(dims)) == 4 * 64 * 24 * 64 * 4
+    pool = torch.tensor([s for s in range(1024) if ((_partition_hash(s) >> 16) & 3) == 0][:80],
+                        dtype=torch.int32)
+    d = scan_case(dev, B=8, H=8, T=24, n_sub=32, d_v=64, W=64, R=64, seed=20)
+    g = torch.Generator().manual_seed(21)
+    n = 8 * 8 * 24
+    for key in ("widx", "ridx"):
+        pick = torch.stack([pool[torch.randperm(80, generator=g)[:64]] for _ in range(n)])
+        d[key] = pick.view(8, 8, 24, 64).contiguous().to(dev)
+    check_scan(d, "overflow with 256 B slices")
 
 
 def test_scans_ignore_slots_outside_the_table(dev):
