@@ -437,10 +437,11 @@ ScanBwdPlan plan_scan_bwd(int S, int T, int64_t N, int d_v, int W, int R) {
          P * 2 <= N)
     P *= 2;
   p.P = P;
-  // registers: mean events of a token in one partition plus four standard
-  // deviations; rarer tokens take the serial path
+  // registers: mean events of a token in one partition plus three standard
+  // deviations; rarer tokens take the serial path, while every register slot
+  // past a token's events is a padding load
   const double mean = (double)(W + R) / P;
-  const double need = mean + 4.0 * sqrt(mean * (1.0 - 1.0 / P)) + 1.0;
+  const double need = mean + 3.0 * sqrt(mean * (1.0 - 1.0 / P));
   const int gpw = 64 / p.lpr;
   p.epl = need <= 4 * gpw ? 4 : need <= 8 * gpw ? 8 : need <= 12 * gpw ? 12 : 16;
   int64_t hs = 1;
