@@ -11,7 +11,8 @@
 //      it (reads see the row after the write).  The sort is a least
 //      significant digit radix sort of the slot, at most 10 bits per pass: a
 //      per-tile digit count, one exclusive sum over (stream, digit, tile),
-//      and a stable scatter that ranks a row of 64 events at once;
+//      and a stable scatter that sorts each tile by digit in LDS (ranking a
+//      row of 64 events at once) before writing it out;
 //   2. one lane group per slot segment loads the row once, applies its writes
 //      in time order with the same roundings as the sequential scan, stores
 //      the row it holds at each read into a read buffer [S][T][R][d_v], and
@@ -37,7 +38,7 @@ namespace {
 constexpr int kSegChunk = 128;  // events per lane group's chunk
 constexpr int kMaxDigit = 10;   // slot bits per sort pass
 constexpr int kMaxRad = 1 << kMaxDigit;
-constexpr int kTile = 4096;     // events per sort tile (one wave each)
+constexpr int kTile = 4096;     // events per sort tile
 
 // One pass of the slot sort: digit (slot >> shift) & (rad - 1) over tiles of
 // kTile events of a stream.
