@@ -123,6 +123,23 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
     const float* V = Q + kTC * kD;
     const float* AB = V + kTC * kD;
     const int nt = min(kTC, a.T - tc0);
+    // k . q of each of the chunk's tokens, computed once (32 threads a token)
+    // into the third slot of its gates instead of by every thread per token
+    {
+      const int tt = tid >> 5, sub = tid & 31;
+      float d = 0.f;
+      if (tt < nt) {
+        const float4 kx = ld4(K + tt * kD + 4 * sub), qx = ld4(Q + tt * kD + 4 * sub);
+        d = fmaf(kx.x, qx.x, d);
+        d = fmaf(kx.y, qx.y, d);
+        d = fmaf(kx.z, qx.z, d);
+        d = fmaf(kx.w, qx.w, d);
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) d += xor_shuffle(d, o, lane);
+      if (sub == 0 && tt < nt) stage[cb][3 * kTC * kD + tt * 4 + 2] = d;
+    }
+    __syncthreads();
     for (int tt = 0; tt < nt; tt++) {
       const float4 k0 = ld4(K + tt * kD + 8 * cg), k1 = ld4(K + tt * kD + 8 * cg + 4);
       const float4 q0 = ld4(Q + tt * kD + 8 * cg), q1 = ld4(Q + tt * kD + 8 * cg + 4);
@@ -142,9 +159,7 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
         val[i] = p;
         val[4 + i] = r;
       }
-      float kq = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; j++) kq = fmaf(kk[j], qq[j], kq);
+      const float kq = AB[tt * 4 + 2];
       // reduce-scatter over the 16 column tiles: lane keeps value 4b3+2b2+b1
       float h4[4];
 #pragma unroll
@@ -167,10 +182,6 @@ __global__ void __launch_bounds__(kThr, 1) sdm_gdn_kernel(GdnArgs a) {
         h1 = keep + xor_shuffle(send, 2, lane);
       }
       h1 += xor_shuffle(h1, 1, lane);
-      kq += xor_shuffle(kq, 1, lane);
-      kq += xor_shuffle(kq, 2, lane);
-      kq += xor_shuffle(kq, 4, lane);
-      kq += xor_shuffle(kq, 8, lane);
       // lane holds row ri = 2b2+b1 of the tile: p if b3 == 0, r if b3 == 1
       // (h1 is of the scaled state: the true p or r is A * h1)
       const int ri = 2 * b2 + b1;
