@@ -201,6 +201,7 @@ def check_scan(d, label):
                                       hot=600)),
     ("256 B slices, 16 streams, bf16 v, T=1", dict(B=4, H=4, T=1, n_sub=32, d_v=128, W=128,
                                                    R=128, seed=19, v_bf16=True)),
+    ("N=33^2, not a power of two", dict(B=2, H=3, T=75, n_sub=33, d_v=64, W=24, R=40, seed=22)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=64, d_v=32, W=4, R=4, seed=7)),
     ("small table, T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
 ])

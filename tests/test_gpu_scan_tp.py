@@ -61,6 +61,10 @@ def scan_case(dev, B, H, T, n_sub, d_v, W, R, seed, v_bf16=False, hot=None):
     ("W=R=128, d_v=256", dict(B=2, H=2, T=40, n_sub=32, d_v=256, W=128, R=128, seed=6,
                               hot=300)),
     ("T=1", dict(B=1, H=1, T=1, n_sub=8, d_v=32, W=4, R=4, seed=7)),
+    # N = 1089 needs 11 slot bits: two passes of 6-bit digits
+    ("N=33^2, two 6-bit passes", dict(B=2, H=2, T=90, n_sub=33, d_v=64, W=24, R=40, seed=8)),
+    # N = 16: one 4-bit pass, every slot hot
+    ("N=16", dict(B=1, H=3, T=64, n_sub=4, d_v=16, W=5, R=7, seed=9)),
 ])
 def test_timeparallel_equals_oracle_bitwise(dev, label, args):
     say(f"case: time-parallel scan {label}", args)
