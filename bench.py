@@ -266,6 +266,27 @@ def bench_decode(args, wl, dev):
     g.replay()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
+    # the same steps fused into one launch each (sdm_decode_step), timed the same way
+    fbufs = {}
+
+    def fstep(tk):
+        sdm.decode_step_fused(M, xd["q"][tk], xd["k"][tk], xd["subkeys"], xd["v"][tk],
+                              xd["alpha"][tk], xd["beta"][tk], wl.W, wl.R, packed=packed,
+                              bufs=fbufs)
+
+    fstep(Wm)
+    torch.cuda.synchronize()
+    gf = torch.cuda.CUDAGraph()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gf, stream=cap):
+            for i in range(K):
+                fstep(Wm + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gf.replay()
+    torch.cuda.synchronize()
+    ms_fused = (time.perf_counter() - t0) * 1e3 / K
     value = wl.streams / (ms_step * 1e-3)
     sbytes = wl.streams * scan_bytes_per_token(wl)
     achieved = sbytes / (ms_scan * 1e-3) / 1e9
@@ -287,7 +308,9 @@ def bench_decode(args, wl, dev):
             "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "kernels": {"score_topk_ms": round(ms_score, 5), "scan_ms": round(ms_scan, 5),
-                        "eager_wall_ms_per_step": round(eager_ms, 5)}}
+                        "eager_wall_ms_per_step": round(eager_ms, 5),
+                        "fused_ms_per_step": round(ms_fused, 5),
+                        "fused_tokens_per_s": round(wl.streams / (ms_fused * 1e-3), 1)}}
     print(json.dumps(line), flush=True)
 
 

@@ -150,6 +150,36 @@ int sdm_score_topk_packed(const sdm_dims* dims, sdm_dtype in_dtype, const void* 
                           size_t workspace_bytes, void* stream);
 
 /*
+ * sdm_decode_step -- one decoding step in one launch: sdm_score_topk_packed's
+ * addressing of one new token per stream, then, in the same workgroups, that
+ * token's gated delta write and sparse read as sdm_scan does them (Spanish
+ * page "Mecanismo Central" items 2 to 4).
+ *
+ * dims describe the addressing problem; every one of its B*H*T tokens is a
+ * scan stream of its own holding that one token: token t of addressing stream
+ * st = b*H + h is scan stream s = st*T + t.  For the decoding layout (dims
+ * B = 1, H heads, T = the batch of sequences), s = h*T + t, i.e. head-major
+ * [H][batch] streams, as sdm_scan sees them when decoding.
+ *   qp, kp, subkeys, widx, wwt, ridx, rwt, workspace   as sdm_score_topk_packed
+ *                            (slot lists and weights are written, [S][T][W/R])
+ *   M      [B*H*T][N][d_v]  fp32      in/out, the streams' tables
+ *   v      [B*H*T][d_v]     v_dtype
+ *   alpha, beta [B*H*T]     fp32
+ *   out    [B*H*T][d_v]     fp32      the read of each token
+ * Tables are bit-identical to sdm_score_topk_packed followed by sdm_scan (the
+ * same write in the same roundings); outputs agree with sdm_scan's to fp32
+ * rounding (the read is summed in another order).  Slots outside [0, N) are
+ * ignored as in sdm_scan.  Limits: those of sdm_score_topk, and d_v one of
+ * 16, 32, 64, 128, 256 (else SDM_ERR_UNSUPPORTED); M, v and out 16-byte
+ * aligned.
+ */
+int sdm_decode_step(const sdm_dims* dims, sdm_dtype in_dtype, const void* qp, const void* kp,
+                    const void* subkeys, sdm_dtype v_dtype, float* M, const void* v,
+                    const float* alpha, const float* beta, int32_t* widx, float* wwt,
+                    int32_t* ridx, float* rwt, float* out, const void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * sdm_scan -- sparse gated-delta write and sparse read over the memory table
  * (Spanish page "Mecanismo Central" items 1, 3 and 4; French page
  * "Mecanisme Central").

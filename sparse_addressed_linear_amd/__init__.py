@@ -24,7 +24,7 @@ STATUS = {0: "SDM_OK", 1: "SDM_ERR_NULL", 2: "SDM_ERR_SHAPE", 3: "SDM_ERR_DTYPE"
           4: "SDM_ERR_UNSUPPORTED", 5: "SDM_ERR_ALIGN", 6: "SDM_ERR_HIP",
           7: "SDM_ERR_WORKSPACE", 8: "SDM_ERR_SCRATCH"}
 EXPORTS = ("sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-           "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_scan",
+           "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_decode_step", "sdm_scan",
            "sdm_scan_workspace_size", "sdm_scan_record",
            "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
            "sdm_score_topk_backward_workspace_size",
@@ -62,6 +62,8 @@ def lib():
         L.sdm_pack_subkeys.restype = ctypes.c_int
         L.sdm_score_topk_packed.argtypes = [PD, I32, P, P, P, P, P, P, P, P, SZ, P]
         L.sdm_score_topk_packed.restype = ctypes.c_int
+        L.sdm_decode_step.argtypes = [PD, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.sdm_decode_step.restype = ctypes.c_int
         L.sdm_score_topk_noalloc.argtypes = [PD, I32, P, P, P, P, P, P, P, P]
         L.sdm_score_topk_noalloc.restype = ctypes.c_int
         L.sdm_score_topk_workspace_size.argtypes = [PD, I32]
@@ -435,6 +437,49 @@ def decode_step(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, bufs=None
                rwt.view(H, B, 1, R), v.view(H, B, 1, d_v), alpha.view(H, B, 1),
                beta.view(H, B, 1), out=bufs["out"], workspace=bufs.get("scan_ws"), stream=stream)
     return out.view(H, B, d_v)
+
+
+def decode_step_fused(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, bufs=None,
+                      stream=None):
+    """decode_step in one launch (sdm_decode_step): the same layouts and
+    arguments; tables bit-identical to decode_step's, outputs equal to fp32
+    rounding.  ``packed`` is ``pack_subkeys(subkeys)`` (packed here on every
+    call when None and the sub-keys are bf16).  Returns out [H,B,d_v] fp32."""
+    H, B, N, d_v = M.shape
+    d_k = qp.shape[-1]
+    n_sub = int(round(N ** 0.5))
+    if n_sub * n_sub != N:
+        raise ValueError("N must be n_sub^2")
+    if qp.shape != (H, B, d_k) or kp.shape != qp.shape or v.shape != (H, B, d_v) or \
+            alpha.shape != (H, B) or beta.shape != (H, B) or subkeys.shape != (H, 2, n_sub, d_k // 2):
+        raise ValueError("shape mismatch in decode_step_fused arguments")
+    bufs = {} if bufs is None else bufs
+    dev = M.device
+    if "idx" not in bufs:
+        bufs["idx"] = (torch.empty((1, H, B, W), dtype=torch.int32, device=dev),
+                       torch.empty((1, H, B, W), dtype=torch.float32, device=dev),
+                       torch.empty((1, H, B, R), dtype=torch.int32, device=dev),
+                       torch.empty((1, H, B, R), dtype=torch.float32, device=dev))
+        bufs["out"] = torch.empty((H, B, d_v), dtype=torch.float32, device=dev)
+    if packed is None and subkeys.dtype == torch.bfloat16:
+        packed = pack_subkeys(subkeys, stream=stream)
+    dt = _dtype_code(qp)
+    if _dtype_code(kp) != dt or _dtype_code(subkeys) != dt:
+        raise ValueError("qp, kp and subkeys must share one dtype")
+    d = Dims(1, H, B, d_k, n_sub, d_v, W, R)
+    need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
+    wsp = _dev(packed, "packed") if need else ctypes.c_void_p(0)
+    widx, wwt, ridx, rwt = bufs["idx"]
+    out = bufs["out"]
+    rc = lib().sdm_decode_step(
+        ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
+        _dtype_code(v), _dev(M, "M", torch.float32), _dev(v, "v"),
+        _dev(alpha, "alpha", torch.float32), _dev(beta, "beta", torch.float32),
+        _dev(widx, "widx", torch.int32), _dev(wwt, "wwt", torch.float32),
+        _dev(ridx, "ridx", torch.int32), _dev(rwt, "rwt", torch.float32),
+        _dev(out, "out", torch.float32), wsp, ctypes.c_size_t(need), _stream(stream))
+    _check("sdm_decode_step", rc)
+    return out
 
 
 def route_topk(zk, zq, a, K, stream=None):

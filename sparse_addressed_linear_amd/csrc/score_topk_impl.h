@@ -39,6 +39,7 @@
 
 #include <type_traits>
 
+#include "scan_common.h"
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -663,12 +664,29 @@ struct ScoreZ {
 // more of the dependent latency of the sorts and stage 2 than the spills cost.
 // Larger grids need more LDS (two workgroups a CU either way) and decoding
 // launches use too few workgroups for occupancy to matter: there 128 VGPRs.
+// The fused decoding step's gated delta write of one element, as the scan's:
+// c = beta*w, then (1-c)*(alpha*m) + c*v, every product and the sum rounded
+// separately (no contraction), so tables match the scan's bit for bit.
+__device__ __forceinline__ void dec_gate(float beta, float w, float& c, float& omc) {
+#pragma clang fp contract(off)
+  c = beta * w;
+  omc = 1.0f - c;
+}
+
+__device__ __forceinline__ float dec_upd(float m, float al, float omc, float c, float v) {
+#pragma clang fp contract(off)
+  const float mt = al * m;
+  const float keep = omc * mt;
+  const float put = c * v;
+  return keep + put;
+}
+
 template <int NPL2, int TT>
 constexpr bool score_high_occ() {
   return TT == kTT && NPL2 <= 5;
 }
 
-template <bool BF16, int NT, int NPL2, int TT>
+template <bool BF16, int NT, int NPL2, int TT, bool FUSE>
 __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4))
     sdm_score_topk_kernel(ScoreArgs a, int tiles_per_wg, ScoreZ z) {
   static_assert(TT == kTT || TT == kTT / 2, "tile of 8 or 4 tokens");
@@ -887,6 +905,82 @@ __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4)
                      (q ? a.rwt : a.wwt) + ((int64_t)st * a.T + tw) * k);
       }
     }
+
+    // ---- 4. fused decoding step: each token of the tile is a stream of its
+    // own holding this one token.  The wave owning a token's key column
+    // applies its gated delta writes; after a barrier, the wave owning its
+    // query column sums its reads, taken after the write (Spanish page
+    // "Mecanismo Central" items 3 and 4).  A lane group of d_v/4 lanes takes
+    // one row at a time, 8 rows' loads in flight.  A build of its own (FUSE,
+    // 4-token tiles), so that the other builds' registers are not touched.
+    if constexpr (FUSE) {
+      static_assert(!FUSE || TT == kTT / 2, "the fused step takes 4-token tiles");
+      __syncthreads();  // the tile's slot lists are written
+      const int lpr = a.d_v >> 2;  // a power of two, at most 64
+      const int gpw = 64 / lpr;
+      const int rg = lane / lpr, rl = lane - rg * lpr;
+      // 4-token tiles: waves 0-3 own the tokens' key columns, 4-7 their query
+      // columns (one each)
+      const int cc = owned(wave, 0);
+      const bool isq = cc >= kTT;
+      const int tw = t0 + (cc & (kTT - 1));
+      const bool live = (cc & (kTT - 1)) < TT && tw < a.T;  // wave-uniform
+      const int64_t s = (int64_t)st * a.T + tw;  // slot-list row and stream of the token
+      const int K = isq ? a.R : a.W;
+      const int32_t* idx = (isq ? a.ridx : a.widx) + s * K;
+      const float* wt = (isq ? a.rwt : a.wwt) + s * K;
+      float* Ms = a.M + s * a.N * a.d_v + 4 * rl;
+      // rows in batches of kEB per lane group, every row load of a batch in
+      // flight before its first use (positions past the list, or naming no
+      // slot of the table, load row 0 and are not used)
+      constexpr int kEB = 8;
+      for (int ph = 0; ph < 2; ph++) {  // 0: the writes, 1: the reads
+        if (live && isq == (ph == 1)) {
+          float al = 0.f, be = 0.f;
+          float4 vv = make_float4(0.f, 0.f, 0.f, 0.f), acc = vv;
+          if (ph == 0) {
+            al = a.alpha[s];
+            be = a.beta[s];
+            vv = scanc::load_v4(a.v, a.v_bf16 != 0, s * a.d_v + 4 * rl);
+          }
+          for (int j0 = rg; j0 < K; j0 += gpw * kEB) {
+            int32_t sl[kEB];
+            float wv[kEB];
+            float4 m[kEB];
+#pragma unroll
+            for (int u = 0; u < kEB; u++) {
+              const int j = j0 + u * gpw;
+              sl[u] = j < K ? idx[j] : -1;
+              wv[u] = j < K ? wt[j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kEB; u++) {
+              const bool ok = (uint32_t)sl[u] < (uint32_t)a.N;
+              m[u] = *reinterpret_cast<const float4*>(Ms + (int64_t)(ok ? sl[u] : 0) * a.d_v);
+            }
+#pragma unroll
+            for (int u = 0; u < kEB; u++) {
+              if ((uint32_t)sl[u] >= (uint32_t)a.N) continue;
+              if (ph == 0) {
+                float c, omc;
+                dec_gate(be, wv[u], c, omc);
+                *reinterpret_cast<float4*>(Ms + (int64_t)sl[u] * a.d_v) = make_float4(
+                    dec_upd(m[u].x, al, omc, c, vv.x), dec_upd(m[u].y, al, omc, c, vv.y),
+                    dec_upd(m[u].z, al, omc, c, vv.z), dec_upd(m[u].w, al, omc, c, vv.w));
+              } else {
+                acc = scanc::fma4(wv[u], m[u], acc);
+              }
+            }
+          }
+          if (ph == 1) {
+            for (int off = lpr; off < 64; off <<= 1)
+              acc = scanc::add4(acc, scanc::shfl_xor4(acc, off));
+            if (rg == 0) *reinterpret_cast<float4*>(a.out + s * a.d_v + 4 * rl) = acc;
+          }
+        }
+        __syncthreads();  // writes before reads; reads before the next tile's lists
+      }
+    }
   }
 }
 
@@ -936,14 +1030,16 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   // tiles of 8 tokens unless they would leave CUs idle (decoding, short
   // sequences): then tiles of 4, twice the workgroups, shorter per-tile chains
   const bool small = (int64_t)((a.T + kTT - 1) / kTT) * a.S < kTargetWorkgroups;
-  auto k = small ? sdm_score_topk_kernel<BF16, NT, NPL2, kTT / 2>
-                 : sdm_score_topk_kernel<BF16, NT, NPL2, kTT>;
+  // the fused decoding step always takes 4-token tiles
+  auto k = a.fuse ? sdm_score_topk_kernel<BF16, NT, NPL2, kTT / 2, true>
+                  : small ? sdm_score_topk_kernel<BF16, NT, NPL2, kTT / 2, false>
+                          : sdm_score_topk_kernel<BF16, NT, NPL2, kTT, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
   // token tiles per workgroup: up to 4 (one grid build serves them all)
   // while the launch still has at least 2048 workgroups
-  const int tt = small ? kTT / 2 : kTT;
+  const int tt = (small || a.fuse) ? kTT / 2 : kTT;
   const int ntiles = (a.T + tt - 1) / tt;
   int per = 1;
   while (per < 4 && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;

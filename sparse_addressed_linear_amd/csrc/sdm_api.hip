@@ -158,6 +158,53 @@ int sdm_score_topk_packed(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
                    workspace_bytes, false, stream);
 }
 
+int sdm_decode_step(const sdm_dims* d, sdm_dtype in_dtype, const void* qp, const void* kp,
+                    const void* subkeys, sdm_dtype v_dtype, float* M, const void* v,
+                    const float* alpha, const float* beta, int32_t* widx, float* wwt,
+                    int32_t* ridx, float* rwt, float* out, const void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = check_score(d, in_dtype, qp, kp, subkeys, widx, wwt, ridx, rwt);
+  if (rc) return rc;
+  if (d->T > 0 && (!M || !v || !alpha || !beta || !out)) return SDM_ERR_NULL;
+  if (!valid_dtype(v_dtype)) return SDM_ERR_DTYPE;
+  // one lane group of d_v/4 lanes per row (a power of two dividing 64)
+  if (d->d_v != 16 && d->d_v != 32 && d->d_v != 64 && d->d_v != 128 && d->d_v != 256)
+    return SDM_ERR_UNSUPPORTED;
+  if (d->T == 0) return SDM_OK;
+  const size_t need =
+      sdm::score_topk_workspace_bytes(d->H, d->n_sub, d->d_k, in_dtype == SDM_BF16);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SDM_ERR_WORKSPACE;
+  if ((need > 0 && !aligned16(workspace)) || !aligned16(M) || !aligned16(v) || !aligned16(out))
+    return SDM_ERR_ALIGN;
+  sdm::ScoreArgs a{};
+  a.packed = const_cast<void*>(workspace);  // read only: the sub-keys are packed already
+  a.qp = qp;
+  a.kp = kp;
+  a.subkeys = subkeys;
+  a.widx = widx;
+  a.wwt = wwt;
+  a.ridx = ridx;
+  a.rwt = rwt;
+  a.S = d->B * d->H;
+  a.H = d->H;
+  a.T = d->T;
+  a.d_k = d->d_k;
+  a.n_sub = d->n_sub;
+  a.W = d->W;
+  a.R = d->R;
+  a.M = M;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.N = (int64_t)d->n_sub * d->n_sub;
+  a.d_v = d->d_v;
+  a.v_bf16 = v_dtype == SDM_BF16 ? 1 : 0;
+  a.fuse = 1;
+  hipError_t e = sdm::launch_score_topk(a, in_dtype == SDM_BF16, false, (hipStream_t)stream);
+  return e == hipSuccess ? SDM_OK : SDM_ERR_HIP;
+}
+
 int sdm_score_topk_noalloc(const sdm_dims* d, sdm_dtype in_dtype, const void* qp,
                            const void* kp, const void* subkeys, int32_t* widx, float* wwt,
                            int32_t* ridx, float* rwt, void* stream) {

@@ -204,6 +204,15 @@ struct ScoreArgs {
   int32_t* ridx;           // [S][T][R]
   float* rwt;
   int32_t S, H, T, d_k, n_sub, W, R;
+  // fused decoding step (fuse != 0): token t of addressing stream st is scan
+  // stream st*T + t with one token, table M + (st*T + t)*N*d_v
+  float* M;
+  const void* v;           // [S*T][d_v] (bf16 when v_bf16)
+  const float* alpha;      // [S*T]
+  const float* beta;
+  float* out;              // [S*T][d_v]
+  int64_t N;
+  int32_t d_v, v_bf16, fuse;
 };
 
 // pack: repack the bf16 sub-keys into `packed` first (else it already holds them)

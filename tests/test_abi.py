@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted(
         ["sdm_score_topk", "sdm_score_topk_workspace_size", "sdm_pack_subkeys",
-         "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_scan",
+         "sdm_score_topk_packed", "sdm_score_topk_noalloc", "sdm_decode_step", "sdm_scan",
          "sdm_scan_workspace_size", "sdm_scan_record",
          "sdm_scan_backward", "sdm_scan_backward_workspace_size", "sdm_score_topk_backward",
          "sdm_score_topk_backward_workspace_size",
@@ -300,6 +300,34 @@ def test_score_topk_noalloc_rejects_on_the_host(L):
     # 16 heads of that size fit exactly
     assert L.sdm_score_topk_workspace_size(ctypes.byref(dims(H=16, d_k=512, n_sub=1024, W=64,
                                                               R=64)), 1) == 16 << 20
+
+
+def test_decode_step_rejects_on_the_host(L):
+    """Validation before any launch: addressing arguments as sdm_score_topk's,
+    the scan's tensors, v's type, d_v a power of two in [16, 256], the packed
+    sub-keys as workspace for bf16 inputs, 16-byte alignment."""
+    def step(d, dt=1, vdt=1, null_at=None, ws=P, wsb=1 << 30, m=P):
+        args = [P] * 15
+        args[6] = m
+        if null_at is not None:
+            args[null_at] = ctypes.c_void_p(0)
+        q, k, sk = args[0:3]
+        M, v, al, be, wi, ww, ri, rw, out = args[6:15]
+        return L.sdm_decode_step(ctypes.byref(d), dt, q, k, sk, vdt, M, v, al, be, wi, ww, ri,
+                                 rw, out, ws, ctypes.c_size_t(wsb), None)
+    d = dims(d_v=64)
+    for i in (0, 1, 2, 6, 7, 8, 9, 10, 11, 12, 13, 14):
+        assert step(d, null_at=i) == 1, i
+    assert step(d, dt=5) == 3
+    assert step(d, vdt=5) == 3
+    assert step(dims(d_v=48)) == 4
+    assert step(dims(d_v=512)) == 4
+    assert step(d, ws=ctypes.c_void_p(0)) == 7
+    assert step(d, wsb=16) == 7
+    assert step(d, m=ctypes.c_void_p(4100)) == 5
+    # fp32 inputs need no packed tables
+    assert step(d, dt=0, ws=ctypes.c_void_p(0), wsb=0, m=ctypes.c_void_p(4100)) == 5
+    assert step(dims(d_v=64, T=0), null_at=6) == 0
 
 
 def test_scan_plan_partitions(L):

@@ -156,3 +156,78 @@ def test_decode_graph_replays_match_eager(dev):
         assert torch.equal(bA["out"], bB["out"]), f"replay {r}: outputs differ"
         for j in range(4):
             assert torch.equal(bA["idx"][j], bB["idx"][j]), f"replay {r}: slot list {j} differs"
+
+
+def test_fused_decode_step_equals_two_calls(dev):
+    """sdm_decode_step (one launch) against decode_step (addressing, then the
+    scan), step by step on the same inputs: slot lists and weights
+    bit-identical (the same addressing), tables bit-identical (the same write
+    in the same roundings), outputs within 1e-5 + 1e-4|ref| (the read is
+    summed in another order).  10 sequences per head: a ragged last tile."""
+    wl = synth.WORKLOADS["decode"].with_(B=10, H=3, T=5, n_sub=256, W=32, R=24)
+    say("case: fused decode vs two calls", wl)
+    x = synth.make_inputs(wl, device=dev, with_m0=False)
+    xd = synth.decode_layout(x)
+    M_a = synth.make_m0(wl, dev, head_major=True)
+    M_b = M_a.clone()
+    packed = sdm().pack_subkeys(x["subkeys"])
+    ba, bb = {}, {}
+    for t in range(wl.T):
+        args = (xd["q"][t], xd["k"][t], xd["subkeys"], xd["v"][t], xd["alpha"][t],
+                xd["beta"][t], wl.W, wl.R)
+        oa = sdm().decode_step(M_a, *args, packed=packed, bufs=ba)
+        ob = sdm().decode_step_fused(M_b, *args, packed=packed, bufs=bb)
+        torch.cuda.synchronize()
+        for j in range(4):
+            assert torch.equal(ba["idx"][j], bb["idx"][j]), f"step {t}: slot list {j} differs"
+        assert np.all(close(np_(ob), np_(oa))), f"step {t}: outputs differ"
+    assert torch.equal(M_a, M_b), "tables differ"
+    # without pre-packed tables the binding packs them on every call
+    ob2 = sdm().decode_step_fused(M_b.clone(), *args, bufs={})
+    torch.cuda.synchronize()
+    assert ob2.shape == ob.shape
+
+
+def test_fused_decode_step_fp32_against_oracle(dev):
+    """fp32 inputs are scored in the oracle's order, so every slot equals the
+    oracle's; weights, tables and outputs are then within 1e-5 + 1e-4|ref| of
+    the oracle's own addressing and scan (the weights' exponentials round
+    differently, and the writes use them).  d_v = 16, W = R = 8, a random
+    initial table, 6 sequences per head (a ragged second tile), three steps."""
+    wl = synth.WORKLOADS["tiny"].with_(B=6, H=2, T=3)
+    say("case: fused decode fp32 vs oracle", wl)
+    x = synth.make_inputs(wl, device=dev, with_m0=False)
+    xd = synth.decode_layout(x)
+    g = torch.Generator().manual_seed(41)
+    M = (torch.randn(wl.H, wl.B, wl.N, wl.d_v, generator=g) * 0.1).to(dev)
+    M0 = np_(M).copy()
+    bufs = {}
+    outs, idx = [], [[], [], [], []]
+    for t in range(wl.T):
+        o = sdm().decode_step_fused(M, xd["q"][t], xd["k"][t], xd["subkeys"], xd["v"][t],
+                                    xd["alpha"][t], xd["beta"][t], wl.W, wl.R, bufs=bufs)
+        outs.append(np_(o).copy())
+        for j in range(4):
+            idx[j].append(np_(bufs["idx"][j][0]).copy())
+    torch.cuda.synchronize()
+    Mg = np_(M)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            ref = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]),
+                                    np_(x["subkeys"][h:h + 1]), wl.W, wl.R)
+            for j, key in enumerate(("widx", "wwt", "ridx", "rwt")):
+                got = np.stack([idx[j][t][h, b] for t in range(wl.T)])
+                if key.endswith("idx"):
+                    assert np.array_equal(got, ref[key][0, 0]), (b, h, key)
+                else:
+                    assert np.all(close(got, ref[key][0, 0])), (b, h, key)
+            M_ref = np.ascontiguousarray(M0[h, b][None, None])
+            o_ref = oracle.scan(M_ref, ref["widx"], ref["wwt"], ref["ridx"], ref["rwt"],
+                                np_(x["v"][sl]), np_(x["alpha"][sl]), np_(x["beta"][sl]))
+            assert np.all(close(Mg[h, b], M_ref[0, 0])), (b, h)
+            untouched = np.ones(wl.N, bool)
+            untouched[ref["widx"][0, 0].ravel()] = False
+            assert np.array_equal(Mg[h, b][untouched], M0[h, b][untouched]), (b, h)
+            got = np.stack([outs[t][h, b] for t in range(wl.T)])
+            assert np.all(close(got, o_ref[0, 0])), (b, h)
