@@ -19,7 +19,7 @@ import torch
 import oracle
 import synth
 from oracle import backward as ob
-from gpu_util import ignored_events, np_, say
+from gpu_util import ignored_events, np_, say, thread_map, workers
 
 pytestmark = pytest.mark.gpu
 
@@ -227,22 +227,28 @@ def test_score_backward_is_deterministic(dev):
 
 def test_training_step_large_sampled(dev):
     """The large workload's forward with tape and both backward calls at full
-    size (N = 2^20, 64 streams).  Two sampled streams run on the oracle's own
-    addressing (their slots and weights are overwritten with the oracle's
-    before the scan) and are checked against the gradient oracle."""
+    size (N = 2^20, 64 streams).  Every stream of the last head, and stream
+    (0, 0), run on the oracle's own addressing (their slots and weights are
+    overwritten with the oracle's before the scan) and are checked against the
+    gradient oracle: the scan's gradients and dq', dk' per stream, and the
+    last head's sub-key gradient, which sums over all of that head's streams."""
     wl = synth.WORKLOADS["large"]
     say("case: large training step, sampled", wl)
     x = synth.make_inputs(wl, device=dev)
     B, H, T = wl.B, wl.H, wl.T
     g = sdm().score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R)
     widx, wwt, ridx, rwt = (t.clone() for t in g)
-    picks = ((0, 0), (B - 1, H - 1))
-    refs = {}
-    for b, h in picks:
+    hl = H - 1
+    picks = [(b, hl) for b in range(B)] + [(0, 0)]
+
+    def addr(p):
+        b, h = p
         sl = (slice(b, b + 1), slice(h, h + 1))
-        r = oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
-                              wl.W, wl.R)
-        refs[(b, h)] = r
+        return oracle.score_topk(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
+                                 wl.W, wl.R)
+
+    refs = dict(zip(picks, thread_map(addr, picks)))
+    for (b, h), r in refs.items():
         for dst, key in ((widx, "widx"), (wwt, "wwt"), (ridx, "ridx"), (rwt, "rwt")):
             dst[b, h] = torch.from_numpy(r[key][0, 0]).to(dev)
     gen = torch.Generator(device=dev).manual_seed(77)
@@ -258,21 +264,33 @@ def test_training_step_large_sampled(dev):
                                            gs["dwwt"], gs["drwt"])
     torch.cuda.synchronize()
     del tape
-    for b, h in picks:
-        assert np.array_equal(np_(M[b, h]), M0[(b, h)]), "table not restored to M0"
-        r = refs[(b, h)]
-        ref = ob.scan_backward_stream(M0[(b, h)], r["widx"][0, 0], r["wwt"][0, 0],
-                                      r["ridx"][0, 0], r["rwt"][0, 0], np_(x["v"][b, h]),
-                                      np_(x["alpha"][b, h]), np_(x["beta"][b, h]),
-                                      np_(dout[b, h]))
-        grad_close(np_(dM[b, h]), ref["dM0"], "large dM0")
-        for key in ("dv", "dalpha", "dbeta", "dwwt", "drwt"):
-            grad_close(np_(gs[key][b, h]), ref[key], f"large {key}")
-        # the addressing adjoint of this stream's tokens (dq', dk' are per token)
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        sref = ob.score_backward(np_(x["q"][sl]), np_(x["k"][sl]), np_(x["subkeys"][h:h + 1]),
-                                 r["widx"], r["ridx"], ref["dwwt"][None, None],
-                                 ref["drwt"][None, None])
-        grad_close(np_(dq[b, h]), sref["dq"][0, 0], "large dq")
-        grad_close(np_(dk[b, h]), sref["dk"][0, 0], "large dk")
     assert torch.isfinite(dC).all()
+    for p in picks:
+        assert np.array_equal(np_(M[p]), M0[p]), f"table of stream {p} not restored to M0"
+    host = {p: {n: np_(x[n][p]) for n in ("v", "alpha", "beta")} | {"dout": np_(dout[p])}
+            for p in picks}
+
+    def rev(p):
+        r = refs[p]
+        return ob.scan_backward_stream(M0[p], r["widx"][0, 0], r["wwt"][0, 0], r["ridx"][0, 0],
+                                       r["rwt"][0, 0], host[p]["v"], host[p]["alpha"],
+                                       host[p]["beta"], host[p]["dout"])
+
+    grads = dict(zip(picks, thread_map(rev, picks, n=min(workers(), 8))))
+    for p in picks:
+        ref = grads[p]
+        grad_close(np_(dM[p]), ref["dM0"], f"large dM0 {p}")
+        for key in ("dv", "dalpha", "dbeta", "dwwt", "drwt"):
+            grad_close(np_(gs[key][p]), ref[key], f"large {key} {p}")
+    # the addressing adjoint: dq', dk' of stream (0, 0); dq', dk' of every
+    # stream of the last head and that head's sub-key gradient
+    for hh, bs in ((0, [0]), (hl, list(range(B)))):
+        sel = (slice(bs[0], bs[-1] + 1), slice(hh, hh + 1))
+        stack = lambda key: np.stack([refs[(b, hh)][key][0] for b in bs])
+        dstack = lambda key: np.stack([grads[(b, hh)][key][None] for b in bs])
+        sref = ob.score_backward(np_(x["q"][sel]), np_(x["k"][sel]), np_(x["subkeys"][hh:hh + 1]),
+                                 stack("widx"), stack("ridx"), dstack("dwwt"), dstack("drwt"))
+        grad_close(np_(dq[sel]), sref["dq"], f"large dq, head {hh}")
+        grad_close(np_(dk[sel]), sref["dk"], f"large dk, head {hh}")
+        if hh == hl:
+            grad_close(np_(dC[hl]), sref["dsubkeys"][0], f"large dsubkeys, head {hl}")
