@@ -469,8 +469,16 @@ def decode_step_fused(M, qp, kp, subkeys, v, alpha, beta, W, R, packed=None, buf
     d = Dims(1, H, B, d_k, n_sub, d_v, W, R)
     need = int(lib().sdm_score_topk_workspace_size(ctypes.byref(d), dt))
     wsp = _dev(packed, "packed") if need else ctypes.c_void_p(0)
+    if need and packed.numel() * packed.element_size() < need:
+        raise ValueError("packed sub-keys are smaller than these sizes need")
     widx, wwt, ridx, rwt = bufs["idx"]
     out = bufs["out"]
+    # buffers kept from an earlier call must still fit this call's sizes
+    _want(widx, (1, H, B, W), "bufs['idx'] write slots")
+    _want(wwt, (1, H, B, W), "bufs['idx'] write weights")
+    _want(ridx, (1, H, B, R), "bufs['idx'] read slots")
+    _want(rwt, (1, H, B, R), "bufs['idx'] read weights")
+    _want(out, (H, B, d_v), "bufs['out']")
     rc = lib().sdm_decode_step(
         ctypes.byref(d), dt, _dev(qp, "qp"), _dev(kp, "kp"), _dev(subkeys, "subkeys"),
         _dtype_code(v), _dev(M, "M", torch.float32), _dev(v, "v"),

@@ -186,6 +186,12 @@ def test_fused_decode_step_equals_two_calls(dev):
     ob2 = sdm().decode_step_fused(M_b.clone(), *args, bufs={})
     torch.cuda.synchronize()
     assert ob2.shape == ob.shape
+    # buffers kept for other sizes, or a packed buffer that is too small, are
+    # refused before any launch
+    with pytest.raises(ValueError):
+        sdm().decode_step_fused(M_b, *args[:-2], wl.W + 8, wl.R, packed=packed, bufs=bb)
+    with pytest.raises(ValueError):
+        sdm().decode_step_fused(M_b, *args, packed=packed[: packed.numel() // 2], bufs=bb)
 
 
 def test_fused_decode_step_fp32_against_oracle(dev):
