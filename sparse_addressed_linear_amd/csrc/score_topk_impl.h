@@ -1037,12 +1037,15 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
-  // token tiles per workgroup: up to 4 (one grid build serves them all)
-  // while the launch still has at least 2048 workgroups
+  // token tiles per workgroup (one grid build serves them all) while the
+  // launch still has at least 2048 workgroups: up to 4, or up to 16 for the
+  // large pruned grids (more than 5 keys a lane, k > 71), whose build costs
+  // more (Long: 11.6 against 12.3 ms with 4)
   const int tt = (small || a.fuse) ? kTT / 2 : kTT;
   const int ntiles = (a.T + tt - 1) / tt;
+  const int per_max = NPL2 <= 5 ? 4 : 16;
   int per = 1;
-  while (per < 4 && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
+  while (per < per_max && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
   dim3 grid((ntiles + per - 1) / per, a.S);
   const ScoreZ z{guess_z(a.W, a.n_sub), guess_z(a.R, a.n_sub), guess_z(a.W, pruned_grid_size(a.W)),
                  guess_z(a.R, pruned_grid_size(a.R))};
