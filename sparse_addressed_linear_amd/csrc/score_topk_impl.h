@@ -1038,12 +1038,12 @@ static inline hipError_t launch_t(const ScoreArgs& a, hipStream_t stream) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   if (e != hipSuccess) return e;
   // token tiles per workgroup (one grid build serves them all) while the
-  // launch still has at least 2048 workgroups: up to 4, or up to 16 for the
+  // launch still has at least 2048 workgroups: up to 8, or up to 16 for the
   // large pruned grids (more than 5 keys a lane, k > 71), whose build costs
-  // more (Long: 11.6 against 12.3 ms with 4)
+  // more (Long: 11.7 against 12.4 ms with 4)
   const int tt = (small || a.fuse) ? kTT / 2 : kTT;
   const int ntiles = (a.T + tt - 1) / tt;
-  const int per_max = NPL2 <= 5 ? 4 : 16;
+  const int per_max = NPL2 <= 5 ? 8 : 16;
   int per = 1;
   while (per < per_max && (int64_t)((ntiles + 2 * per - 1) / (2 * per)) * a.S >= 2048) per *= 2;
   dim3 grid((ntiles + per - 1) / per, a.S);
