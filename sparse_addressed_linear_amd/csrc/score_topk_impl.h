@@ -489,11 +489,12 @@ __device__ __forceinline__ void emit_slots(const uint64_t (&v)[E], int k, int la
 // registers, check the frontier outside the pruned grid, write the result.
 // Returns false when the frontier could compete (the caller then ranks the
 // full grid).
-template <int E>
+template <int E, bool TIEK>
 __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32_t obase,
                                               uint32_t omax, const uint64_t* L1,
                                               const uint64_t* L2, const int32_t* rowoff, int m,
-                                              int k, int lane, int32_t* dst_i, float* dst_w) {
+                                              int k, const uint64_t* lk, int lane,
+                                              int32_t* dst_i, float* dst_w) {
   uint64_t v[E];
   sort_keys<E>(buf, c, lane, obase, omax, v);
   // k-th best key: position k-1 = lane (k-1)/E, register (k-1)%E
@@ -504,32 +505,48 @@ __device__ __forceinline__ bool stage2_sorted(const uint64_t* buf, int c, uint32
   const uint32_t klo = __shfl((uint32_t)kv, src), khi = __shfl((uint32_t)(kv >> 32), src);
   const float kth_score = unord32(khi);
   (void)klo;
-  // best pair just outside the pruned grid, row by row: exact if it cannot
-  // outrank the k-th (compare scores: a score tie with a lower slot would)
+  // best pair just outside the pruned grid within the first k ranks, row by
+  // row: exact if it cannot outrank the k-th (compare scores: a score tie
+  // with a lower slot would)
   float fr = -INFINITY;
   bool any = false;
-  for (int ra = lane; ra < m; ra += 64) {
+  for (int ra = lane; ra < k; ra += 64) {
     const int rb = rowoff[ra + 1] - rowoff[ra];  // row ra of the grid: ranks 0 .. rb-1
-    if (rb < m) {
+    if (rb < k) {
       const float s = entry_score(L1[ra]) + entry_score(L2[rb]);
       fr = any ? fmaxf(fr, s) : s;
       any = true;
     }
   }
-  const bool compete = __ballot(any && !(fr < kth_score)) != 0ull;
+  // the pairs holding a list's rank-k entry (lk[0] of L1, lk[1] of L2;
+  // present when m > k) lie outside the k x k grid: (0, k) and (k, 0) bound
+  // them all, as a sum never grows with either rank
+  bool edge = false;
+  if constexpr (TIEK) {
+    if (m > k) {
+      const float f1 = entry_score(L1[0]) + entry_score(lk[1]);
+      const float f2 = entry_score(lk[0]) + entry_score(L2[0]);
+      edge = !(f1 < kth_score) || !(f2 < kth_score);
+    }
+  }
+  const bool compete = edge || __ballot(any && !(fr < kth_score)) != 0ull;
   if (compete) return false;
   emit_slots<E>(v, k, lane, dst_i, dst_w);
   return true;
 }
 
 // Stage 2 for one column whose stage-1 lists (rank order, list_entry form)
-// are L1, L2: the k best slots over the pruned grid (row offsets rowoff),
-// written in rank order with their softmax weights.  buf holds cap_for(k)
-// keys of scratch.
-template <int NPL2>
-__device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, int m, int k,
-                                       int n_sub, const uint32_t* grid, const int32_t* rowoff,
-                                       int G, float z, uint64_t* buf, int lane, int32_t* dst_i,
+// are L1, L2 (ranks 0 .. k-1) and lk[0], lk[1] (rank k): the k best slots over the
+// pruned grid (row offsets rowoff), written in rank order with their softmax
+// weights.  The selection is defined on the m x m grid of the stage-1 lists
+// (m = k+1, or n_sub when that is smaller); a pair outside the pruned grid
+// can only enter it through an fp32 tie, and then the full m x m grid is
+// ranked.  buf holds cap_for(k) keys of scratch.
+template <int NPL2, bool TIEK>
+__device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, const uint64_t* lk,
+                                       int m, int k, int n_sub,
+                                       const uint32_t* grid, const int32_t* rowoff, int G,
+                                       float z, uint64_t* buf, int lane, int32_t* dst_i,
                                        float* dst_w) {
   uint64_t key[NPL2];
   float sum = 0.f, sq = 0.f;
@@ -562,16 +579,27 @@ __device__ __forceinline__ void stage2(const uint64_t* L1, const uint64_t* L2, i
   wave_lds_sync();
   bool done;
   const uint32_t ob = (uint32_t)(t >> 32);
-  if (c <= 64) done = stage2_sorted<1>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
-  else if (c <= 128) done = stage2_sorted<2>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
-  else done = stage2_sorted<4>(buf, c, ob, mo, L1, L2, rowoff, m, k, lane, dst_i, dst_w);
+  if (c <= 64)
+    done = stage2_sorted<1, TIEK>(buf, c, ob, mo, L1, L2, rowoff, m, k, lk, lane, dst_i, dst_w);
+  else if (c <= 128)
+    done = stage2_sorted<2, TIEK>(buf, c, ob, mo, L1, L2, rowoff, m, k, lk, lane, dst_i, dst_w);
+  else
+    done = stage2_sorted<4, TIEK>(buf, c, ob, mo, L1, L2, rowoff, m, k, lk, lane, dst_i, dst_w);
   if (done) return;
 
   // rare: rank the full m x m grid.  The k-th key of the pruned grid is a
   // lower bound; bisect upward until at most cap keys remain.
   wave_lds_sync();
   auto full_key = [&](int q) {
-    const uint64_t a1 = L1[q / m], a2 = L2[q % m];
+    const int qa = q / m, qb = q % m;
+    uint64_t a1, a2;
+    if constexpr (TIEK) {
+      a1 = qa < k ? L1[qa] : lk[0];
+      a2 = qb < k ? L2[qb] : lk[1];
+    } else {
+      a1 = L1[qa];
+      a2 = L2[qb];
+    }
     return make_key(entry_score(a1) + entry_score(a2), entry_id(a1) * (uint32_t)n_sub + entry_id(a2));
   };
   auto cnt = [&](uint64_t tt) {
@@ -698,6 +726,7 @@ __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4)
   __shared__ uint32_t s_max[kWaves][kCols];   // per wave: largest score part
   __shared__ int s_cnt[2][kWaves][kCols];     // per wave: #{keys >= t}, two rounds
   __shared__ uint32_t s_range[2][kCols];      // per column: score part of t, largest score part
+  __shared__ uint64_t s_last[kCols][2];       // per column and half: the rank-k list entry
   const ScoreSmem L = score_smem(a.W, a.R);
   const int m = L.m, cm = L.capmax;
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem + L.cand);
@@ -733,8 +762,11 @@ __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4)
       const bool is_q = tl >= kTT;
       const int tok = t0 + (tl & (kTT - 1));
       const bool col_ok = (tl & (kTT - 1)) < TT && tok < a.T;
-      const int kc = is_q ? a.R : a.W;
-      const int capc = cap_for(kc);
+      // fp32: stage 1 keeps k+1 entries (at most n_sub), the rank-k one to
+      // bound the pairs just outside stage 2's grid when fp32 sums tie
+      const int kc0 = is_q ? a.R : a.W;
+      const int capc = cap_for(kc0);
+      const int kc = (!BF16 && kc0 < n_sub) ? kc0 + 1 : kc0;
       const float zc = is_q ? z.r1 : z.w1;
       const uint32_t base_id = 16u * hw + 4u * kq;  // sub-key id of this lane's first score
 
@@ -882,8 +914,17 @@ __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4)
           for (int w = 0; w < kWaves; w++) c += s_cnt[fin][w][cc];
           c = min(c, cm);
           uint64_t* lst = cand + cc * 2 * cm + half * m;
-          sort_emit_range(cand + (cc * 2 + half) * cm, c, k, hl, s_range[0][cc], s_range[1][cc],
-                          [&](int r, uint64_t kk) { lst[r] = list_entry(kk); });
+          if constexpr (BF16) {
+            sort_emit_range(cand + (cc * 2 + half) * cm, c, k, hl, s_range[0][cc],
+                            s_range[1][cc], [&](int r, uint64_t kk) { lst[r] = list_entry(kk); });
+          } else {
+            uint64_t* last = &s_last[cc][half];
+            sort_emit_range(cand + (cc * 2 + half) * cm, c, k < a.n_sub ? k + 1 : k, hl,
+                            s_range[0][cc], s_range[1][cc], [&](int r, uint64_t kk) {
+                              if (r < k) lst[r] = list_entry(kk);
+                              else *last = list_entry(kk);
+                            });
+          }
         }
       }
     }
@@ -898,7 +939,8 @@ __global__ void __launch_bounds__(kThreads, (score_high_occ<NPL2, TT>() ? 6 : 4)
         const int k = q ? a.R : a.W;
         const bool own_grid = q && L.gR;
         uint64_t* blk = cand + cc * 2 * cm;
-        stage2<NPL2>(blk, blk + m, k, k, a.n_sub, own_grid ? grid + L.gW : grid,
+        stage2<NPL2, !BF16>(blk, blk + m, &s_last[cc][0], (!BF16 && k < a.n_sub) ? k + 1 : k, k,
+                     a.n_sub, own_grid ? grid + L.gW : grid,
                      own_grid ? rowoff + (m + 1) : rowoff, own_grid ? L.gR : L.gW,
                      q ? z.r2 : z.w2, blk + 2 * m, lane,
                      (q ? a.ridx : a.widx) + ((int64_t)st * a.T + tw) * k,

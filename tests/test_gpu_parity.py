@@ -134,6 +134,33 @@ def test_score_topk_ragged_and_fp32(dev):
     assert np.all(close(np_(wwt), ref["wwt"])) and np.all(close(np_(rwt), ref["rwt"]))
 
 
+@pytest.mark.parametrize("W,R", [(8, 5), (96, 80)], ids=["small grid", "large grid"])
+def test_score_topk_tile_groups_with_ragged_ends(dev, W, R):
+    """Workgroups take groups of token tiles (8 for pruned grids of at most 5
+    keys a lane, 16 for larger ones, while at least 2048 workgroups remain):
+    here 16 streams of 16405 tokens, 2051 tiles of 8, so the last group holds 3
+    tiles and the last tile 5 tokens.  fp32 inputs are scored in the oracle's
+    order: every slot equals the oracle's."""
+    wl = synth.WORKLOADS["tiny"].with_(B=2, H=8, T=16405, n_sub=256, W=W, R=R)
+    say("case: tile groups with ragged ends", wl)
+    x = synth.make_inputs(wl, device=dev, with_m0=False)
+    widx, wwt, ridx, rwt = sdm().score_topk(x["q"], x["k"], x["subkeys"], wl.W, wl.R)
+    torch.cuda.synchronize()
+    q, k, C = np_(x["q"]), np_(x["k"]), np_(x["subkeys"])
+    streams = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+
+    def ref(p):
+        b, h = p
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        return oracle.score_topk(q[sl], k[sl], C[h:h + 1], wl.W, wl.R)
+
+    for (b, h), r in zip(streams, thread_map(ref, streams)):
+        assert np.array_equal(np_(widx[b, h]), r["widx"][0, 0]), f"write slots of {(b, h)}"
+        assert np.array_equal(np_(ridx[b, h]), r["ridx"][0, 0]), f"read slots of {(b, h)}"
+        assert np.all(close(np_(wwt[b, h]), r["wwt"][0, 0])), f"write weights of {(b, h)}"
+        assert np.all(close(np_(rwt[b, h]), r["rwt"][0, 0])), f"read weights of {(b, h)}"
+
+
 # ------------------------------------------------------------------ scan ---
 
 def scan_case(dev, B, H, T, n_sub, d_v, W, R, seed, v_bf16=False, hot=None):
