@@ -95,10 +95,13 @@ def test_tiny_end_to_end(dev):
 
 # ------------------------------------------------------------ addressing ---
 
-def test_score_topk_integer_ties(dev):
-    """Small-integer bf16 inputs: every score is exact on both sides, with many
-    exact ties, so indices must match the oracle exactly (lowest index wins)."""
-    say("case: integer ties")
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_score_topk_integer_ties(dev, dtype):
+    """Small-integer inputs: every score is exact on both sides, with many
+    exact ties, so indices must match the oracle exactly (lowest index wins).
+    In fp32 the ties also reach the stage-1 lists' rank-k entries, which then
+    send stage 2 to the full (k+1) x (k+1) grid."""
+    say(f"case: integer ties, {dtype}")
     g = torch.Generator().manual_seed(7)
     for (B, H, T, d_k, n_sub, W, R) in ((1, 2, 40, 32, 64, 16, 12), (2, 1, 33, 64, 32, 32, 5),
                                         (1, 1, 17, 32, 128, 128, 128),
@@ -112,7 +115,7 @@ def test_score_topk_integer_ties(dev):
         q = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         k = torch.randint(-2, 3, (B, H, T, d_k), generator=g).float()
         C = torch.randint(-1, 2, (H, 2, n_sub, d_k // 2), generator=g).float()
-        qb, kb, Cb = (t.to(torch.bfloat16).to(dev) for t in (q, k, C))
+        qb, kb, Cb = (t.to(dtype).to(dev) for t in (q, k, C))
         say(f"  B={B} H={H} T={T} d_k={d_k} n_sub={n_sub} W={W} R={R}")
         widx, wwt, ridx, rwt = sdm().score_topk(qb, kb, Cb, W, R)
         torch.cuda.synchronize()
