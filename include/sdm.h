@@ -88,6 +88,11 @@ typedef struct {
  *                                   its contents on entry do not matter.
  *
  * Scores are accumulated in fp32 (bf16 products are exact in fp32).
+ * Candidate set: the (k+1) x (k+1) grid of the two halves' top-(k+1) lists.
+ * fp32 inputs are scored in sequential order and ranked on that whole grid,
+ * ties included.  bf16 inputs are scored on the matrix cores, in another
+ * summation order; there a pair holding a half's (k+1)-th sub-key whose fp32
+ * sum exactly ties the k-th selected sum may lose to a higher slot index.
  * Kernel limits (else SDM_ERR_UNSUPPORTED): n_sub a multiple of 16 and
  * <= 1024, d_k/2 a multiple of 16 and <= 256, W, R <= min(n_sub, 128).
  * Inputs must be finite.
